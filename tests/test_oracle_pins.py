@@ -1,0 +1,413 @@
+"""Pins for the CPU oracle: it is checked against things other than itself.
+
+Each test fixes one step of the oracle to a closed form, an invariant, a
+library routine on a special case, brute force on a tiny input, or a worked
+example the pages give, so that a plausible slip (a dropped term, a wrong sign
+or index, a transposed operand) fails at least one of them.
+"""
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import bsa_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------- decoding
+
+def test_e4m3_decode_exhaustive_against_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = O.decode_e4m3(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    m = ~np.isnan(ref)
+    assert np.array_equal(ours[m], ref[m])
+    assert np.nanmax(ours) == 448.0 and np.nanmin(ours) == -448.0
+    assert np.isnan(ours).sum() == 2  # +-NaN only: the fn variant has no infinities
+
+
+def test_bf16_decode_against_torch():
+    rng = np.random.default_rng(1)
+    x = torch.from_numpy(rng.standard_normal(4096).astype(np.float32) * 100).to(torch.bfloat16)
+    bits = x.view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(O.decode_bf16(bits), x.to(torch.float64).numpy())
+
+
+def test_dequantize_uses_head_and_block_scale():
+    S, H, D, B = 10, 2, 3, 4
+    codes = np.full((S, H, D), 0x38, dtype=np.uint8)  # 0x38 = 1.0 in E4M3
+    scales = np.array([[1.0, 2.0, 3.0], [10.0, 20.0, 30.0]])
+    x = O.dequantize(codes, scales, B)
+    assert x[0, 0, 0] == 1.0 and x[4, 0, 1] == 2.0 and x[9, 0, 2] == 3.0
+    assert x[9, 1, 0] == 30.0 and x[3, 1, 0] == 10.0
+
+
+# ---------------------------------------------------------------- pooling
+
+def test_pool_identical_rows_closed_form():
+    rng = np.random.default_rng(2)
+    S, H, D, B = 12, 2, 5, 4
+    rows = rng.standard_normal((S // B, H, D))
+    K = np.repeat(rows, B, axis=0)
+    kbar, r = O.pool_keys(K, B)
+    for g in range(H):
+        assert np.allclose(kbar[g], rows[:, g, :], rtol=0, atol=1e-15)
+        assert np.all(r[g] < 1e-12)
+
+
+def test_pool_radius_plus_minus_closed_form():
+    rng = np.random.default_rng(3)
+    D, B = 6, 4
+    c = rng.standard_normal(D)
+    a = rng.standard_normal(D)
+    K = np.stack([c + a, c - a, c + a, c - a])[:, None, :]
+    kbar, r = O.pool_keys(K, B)
+    assert np.allclose(kbar[0, 0], c, atol=1e-14)
+    assert abs(r[0, 0] - np.linalg.norm(a)) < 1e-12
+
+
+def test_pool_radius_is_max_not_mean():
+    # three keys at the centroid, one far away: the radius is the far key's distance
+    D, B = 4, 4
+    K = np.zeros((4, 1, D))
+    K[3, 0, 0] = 4.0
+    kbar, r = O.pool_keys(K, B)
+    assert np.allclose(kbar[0, 0], [1.0, 0, 0, 0])
+    assert abs(r[0, 0] - 3.0) < 1e-12
+
+
+def test_pool_queries_group_mean_is_mean_of_head_means():
+    rng = np.random.default_rng(4)
+    S, Hq, Hkv, D, B = 16, 4, 2, 3, 8
+    Q = rng.standard_normal((S, Hq, D))
+    per_head, qn_h = O.pool_queries(Q, B, Hkv, "qhead")
+    grp, qn_g = O.pool_queries(Q, B, Hkv, "group")
+    assert np.allclose(grp[0], per_head[0:2].mean(axis=0), atol=1e-15)
+    assert np.allclose(grp[1], per_head[2:4].mean(axis=0), atol=1e-15)
+    assert np.allclose(qn_h, np.linalg.norm(per_head, axis=-1))
+    # block means by hand for one entry
+    assert np.allclose(per_head[3, 1], Q[8:16, 3, :].sum(axis=0) / 8)
+
+
+def test_pool_ragged_last_block_averages_rows_it_has():
+    rng = np.random.default_rng(5)
+    S, B, D = 10, 4, 3
+    K = rng.standard_normal((S, 1, D))
+    kbar, r = O.pool_keys(K, B)
+    assert kbar.shape[1] == 3
+    assert np.allclose(kbar[0, 2], K[8:10, 0].mean(axis=0))
+    Q = rng.standard_normal((S, 1, D))
+    qbar, _ = O.pool_queries(Q, B, 1, "qhead")
+    assert np.allclose(qbar[0, 2], Q[8:10, 0].mean(axis=0))
+
+
+# ---------------------------------------------------------------- scores and bound
+
+def test_scores_bilinear_identity_against_dense_logits():
+    """qbar_i . kbar_j equals the mean of the dense logit block Q_i K_j^T."""
+    rng = np.random.default_rng(6)
+    S, Hq, Hkv, D, B = 40, 4, 2, 8, 8
+    Q = rng.standard_normal((S, Hq, D))
+    K = rng.standard_normal((S, Hkv, D))
+    for gran in ("qhead", "group"):
+        qbar, _ = O.pool_queries(Q, B, Hkv, gran)
+        kbar, _ = O.pool_keys(K, B)
+        s = O.block_scores(qbar, kbar, Hq, Hkv, gran)
+        nb = S // B
+        for u in range(s.shape[0]):
+            heads = [u] if gran == "qhead" else [2 * u, 2 * u + 1]
+            g = u // 2 if gran == "qhead" else u
+            for i in range(nb):
+                for j in range(nb):
+                    if j > i:
+                        assert np.isnan(s[u, i, j])
+                        continue
+                    dense = np.mean([Q[i * B:(i + 1) * B, h] @ K[j * B:(j + 1) * B, g].T for h in heads])
+                    assert abs(s[u, i, j] - dense) < 1e-12
+
+
+def test_rescue_bound_cauchy_schwarz_invariant():
+    rng = np.random.default_rng(7)
+    S, Hq, Hkv, D, B = 64, 2, 1, 8, 8
+    Q = rng.standard_normal((S, Hq, D))
+    K = rng.standard_normal((S, Hkv, D)) * rng.uniform(0.1, 3.0, size=(S, 1, 1))
+    qbar, qn = O.pool_queries(Q, B, Hkv, "qhead")
+    kbar, r = O.pool_keys(K, B)
+    s = O.block_scores(qbar, kbar, Hq, Hkv, "qhead")
+    b = O.rescue_bounds(s, qn, r, Hq, Hkv, "qhead")
+    nb = S // B
+    tight = 0
+    for u in range(Hq):
+        for i in range(nb):
+            for j in range(i + 1):
+                best_key = (K[j * B:(j + 1) * B, 0] @ qbar[u, i]).max()
+                assert b[u, i, j] >= best_key - 1e-12
+                assert b[u, i, j] >= s[u, i, j]
+                tight += b[u, i, j] - best_key < 1e-9
+    # equality when the block's keys are identical (radius 0)
+    K2 = np.repeat(rng.standard_normal((nb, 1, D)), B, axis=0)
+    kbar2, r2 = O.pool_keys(K2, B)
+    s2 = O.block_scores(qbar, kbar2, Hq, Hkv, "qhead")
+    b2 = O.rescue_bounds(s2, qn, r2, Hq, Hkv, "qhead")
+    m = ~np.isnan(s2)
+    assert np.allclose(b2[m], s2[m], atol=1e-12)
+
+
+# ---------------------------------------------------------------- selection
+
+def test_top_k_brute_force_with_ties():
+    rng = np.random.default_rng(8)
+    for trial in range(300):
+        n = int(rng.integers(1, 9))
+        vals = rng.integers(0, 4, size=n).astype(np.float64)  # many exact ties
+        k = int(rng.integers(0, n + 2))
+        got = sorted(O.top_k(vals, list(range(n)), k))
+        kk = min(k, n)
+        best = None
+        for sub in itertools.combinations(range(n), kk):
+            key = (-sum(vals[list(sub)]), sub)
+            if best is None or key < best:
+                best = key
+        assert got == list(best[1]), (vals, k, got, best)
+
+
+def test_top_k_lowest_index_tie_break():
+    vals = np.array([1.0, 5.0, 3.0, 5.0, 3.0, 3.0])
+    assert O.top_k(vals, [0, 1, 2, 3, 4, 5], 3) == [1, 3, 2]
+    assert O.top_k(vals, [0, 2, 4, 5], 2) == [2, 4]
+
+
+def test_gate_two_candidate_closed_form():
+    rng = np.random.default_rng(9)
+    for _ in range(100):
+        a, b = rng.normal(0, 3, size=2)
+        tau = float(rng.uniform(0.1, 2.0))
+        s = np.array([0.0, a, b])  # block 0 forced as sink, candidates {1, 2}
+        gap = O.gate_gap(s, [1, 2], tau)
+        assert abs(gap - math.tanh(tau * abs(a - b) / 2)) < 1e-12
+
+
+def test_gate_worked_example_from_page():
+    fx = json.load(open(os.path.join(GOLDEN, "gate_worked_example.json")))
+    p = O.SelectParams(top_k=fx["top_k"], force_sink=False, gate="top12_gap",
+                       gate_threshold=fx["gate_threshold"], gate_factor=fx["gate_factor"],
+                       score_temperature=fx["score_temperature"]).as_library_precision()
+    # row i = 2: block 2 is the forced diagonal, candidates are blocks 0 and 1
+    s = np.array(fx["scores"] + [0.0])
+    gap = O.gate_gap(s, [0, 1], p.score_temperature)
+    assert abs(gap - math.tanh(0.05)) < 1e-12
+    kept, fired = O.select_row(2, s, None, p)
+    assert fired is fx["expected_fires"]
+    assert kept == sorted(fx["expected_kept_candidates"] + [2])
+    # without the gate the plain top-1 drops the runner-up
+    kept0, _ = O.select_row(2, s, None, O.SelectParams(top_k=1))
+    assert kept0 == [0, 2]
+
+
+def test_gate_does_not_fire_on_clear_winner_and_gated_is_superset():
+    rng = np.random.default_rng(10)
+    p = O.SelectParams(top_k=3, force_sink=True, gate="top12_gap", gate_threshold=0.05)
+    p0 = O.SelectParams(top_k=3, force_sink=True)
+    n_fired = 0
+    for _ in range(200):
+        i = int(rng.integers(1, 30))
+        s = rng.normal(0, float(rng.uniform(0.01, 5)), size=i + 1)
+        kept, fired = O.select_row(i, s, None, p)
+        kept0, _ = O.select_row(i, s, None, p0)
+        assert set(kept0) <= set(kept)
+        _, cands = O.candidate_sets(i, True)
+        assert len(kept) == len(set(kept))
+        expect = min(len(cands), 6 if fired else 3) + (2 if i > 0 else 1)
+        assert len(kept) == expect
+        n_fired += fired
+    assert 0 < n_fired < 200
+    s = np.array([0.0, 10.0, 0.0, 0.0, 0.0])
+    assert not O.select_row(4, s, None, p)[1]
+
+
+def test_mass_prefix_invariants():
+    rng = np.random.default_rng(11)
+    mu = float(np.float32(0.9))
+    for _ in range(200):
+        n = int(rng.integers(1, 40))
+        s = rng.normal(0, float(rng.uniform(0.1, 6)), size=n + 1)
+        order, cum = O.mass_cumulative(s, list(range(n)), 1.0)
+        m = O.mass_prefix_length(cum, mu)
+        p = np.exp(s[:n] - s[:n].max())
+        p /= p.sum()
+        kept = order[:m]
+        assert p[kept].sum() >= mu - 1e-12
+        assert p[kept[:-1]].sum() < mu
+        # kept blocks are exactly the m largest
+        assert set(kept) == set(np.argsort(-s[:n], kind="stable")[:m])
+
+
+def test_mass_single_dominant_block():
+    s = np.array([0.0, 0.0, 8.0, 0.0, 0.0])  # p(block 2) > 0.99
+    p = O.SelectParams(mass_threshold=0.9)
+    kept, _ = O.select_row(4, s, None, p)
+    assert kept == [2, 4]
+
+
+def test_rescue_count_and_ranking_by_bound():
+    assert O.rescue_count(20, 0.05) == 1
+    assert O.rescue_count(21, 0.05) == 2
+    assert O.rescue_count(1, 0.05) == 1
+    assert O.rescue_count(0, 0.05) == 0
+    assert O.rescue_count(1022, 0.05) == 52
+    s = np.zeros(41)
+    b = np.zeros(41)
+    b[[3, 17, 30]] = [5.0, 7.0, 5.0]
+    p = O.SelectParams(rescue_fraction=0.05)  # ceil(0.05 * 40) = 2
+    kept, _ = O.select_row(40, s, b, p)
+    assert kept == [3, 17, 40]
+
+
+def test_union_and_forced_identities():
+    rng = np.random.default_rng(12)
+    p = O.SelectParams(top_k=2, force_sink=True, mass_threshold=0.5, rescue_fraction=0.1)
+    for _ in range(200):
+        i = int(rng.integers(0, 50))
+        s = rng.normal(0, 3, size=i + 1)
+        b = s + rng.uniform(0, 5, size=i + 1)
+        kept, _ = O.select_row(i, s, b, p)
+        forced, cands = O.candidate_sets(i, True)
+        tk = set(O.top_k(s, cands, 2))
+        order, cum = O.mass_cumulative(s, cands, 1.0)
+        base = set(order[:O.mass_prefix_length(cum, 0.5)])
+        resc = set(O.top_k(b, cands, O.rescue_count(len(cands), 0.1)))
+        assert set(kept) == set(forced) | tk | base | resc
+        assert len(kept) <= len(forced) + len(tk) + len(base) + len(resc)
+        assert kept == sorted(set(kept)) and kept[-1] == i and kept[0] == 0
+        assert all(0 <= j <= i for j in kept)
+
+
+def test_csr_round_trip():
+    kept = [[[0], [0, 1], [0, 2]], [[0], [1], [1, 2]]]
+    rp, ci = O.to_csr(kept)
+    assert list(rp) == [0, 1, 3, 5, 6, 7, 9]
+    assert O.from_csr(rp, ci, 2, 3) == kept
+
+
+def test_acceptable_sets_cover_near_threshold():
+    # two candidates whose gate gap sits right at the threshold: both decisions allowed
+    theta = 0.05
+    delta = math.atanh(theta) * 2  # tau*|a-b| so that tanh(.../2) == theta
+    s = np.array([0.0, delta, 0.0])  # row 2: candidates {0, 1}, block 2 forced
+    p = O.SelectParams(top_k=1, gate="top12_gap", gate_threshold=theta)
+    sets, amb = O.acceptable_row_sets(2, s, None, p, 1e-5)
+    assert amb and len(sets) == 2
+    sets, amb = O.acceptable_row_sets(2, np.array([0.0, 3.0, 0.0]), None, p, 1e-5)
+    assert not amb and len(sets) == 1
+
+
+# ---------------------------------------------------------------- attention
+
+def _rand_qkv(rng, S, Hq, Hkv, D):
+    return (rng.standard_normal((S, Hq, D)), rng.standard_normal((S, Hkv, D)),
+            rng.standard_normal((S, Hkv, D)))
+
+
+def test_full_budget_equals_dense_causal_and_sdpa():
+    """With every causal block kept, block-sparse attention is dense causal attention."""
+    rng = np.random.default_rng(13)
+    S, Hq, Hkv, D, B = 50, 4, 2, 8, 8  # ragged last block (50 = 6*8 + 2)
+    Q, K, V = _rand_qkv(rng, S, Hq, Hkv, D)
+    nb = -(-S // B)
+    kept = [[list(range(i + 1)) for i in range(nb)] for _ in range(Hq)]
+    scale = 1 / math.sqrt(D)
+    Os, lse_s = O.attention(Q, K, V, kept, B, scale, "qhead")
+    Od, lse_d = O.dense_causal_attention(Q, K, V, scale)
+    assert np.allclose(Os, Od, atol=1e-12) and np.allclose(lse_s, lse_d, atol=1e-12)
+    qt = torch.from_numpy(Q).permute(1, 0, 2)
+    kt = torch.from_numpy(K).permute(1, 0, 2).repeat_interleave(Hq // Hkv, 0)
+    vt = torch.from_numpy(V).permute(1, 0, 2).repeat_interleave(Hq // Hkv, 0)
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True, scale=scale)
+    assert np.allclose(Os, ref.permute(1, 0, 2).numpy(), atol=1e-12)
+    # lse against torch.logsumexp of the masked logits
+    lg = scale * torch.einsum("hsd,htd->hst", qt, kt)
+    lg = lg.masked_fill(~torch.tril(torch.ones(S, S, dtype=torch.bool)), float("-inf"))
+    assert np.allclose(lse_s, torch.logsumexp(lg, dim=-1).numpy(), atol=1e-12)
+
+
+def test_sparse_mask_matches_sdpa_with_explicit_mask():
+    rng = np.random.default_rng(14)
+    S, Hq, Hkv, D, B = 48, 2, 1, 8, 8
+    Q, K, V = _rand_qkv(rng, S, Hq, Hkv, D)
+    nb = S // B
+    kept = [[sorted({i} | set(rng.choice(i + 1, size=min(i + 1, 2), replace=False).tolist()))
+             for i in range(nb)] for _ in range(Hq)]
+    scale = 0.3
+    Os, _ = O.attention(Q, K, V, kept, B, scale, "qhead")
+    for h in range(Hq):
+        allow = torch.zeros(S, S, dtype=torch.bool)
+        for i in range(nb):
+            for j in kept[h][i]:
+                allow[i * B:(i + 1) * B, j * B:(j + 1) * B] = True
+        allow &= torch.tril(torch.ones(S, S, dtype=torch.bool))
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(Q[:, h])[None], torch.from_numpy(K[:, 0])[None],
+            torch.from_numpy(V[:, 0])[None], attn_mask=allow[None], scale=scale)[0]
+        assert np.allclose(Os[:, h], ref.numpy(), atol=1e-12)
+
+
+def test_attention_row_invariants():
+    rng = np.random.default_rng(15)
+    S, Hq, Hkv, D, B = 32, 2, 2, 4, 8
+    Q, K, V = _rand_qkv(rng, S, Hq, Hkv, D)
+    nb = S // B
+    kept = [[[0, i] if i else [0] for i in range(nb)] for _ in range(Hq)]
+    Os, _ = O.attention(Q, K, V, kept, B, 0.5, "qhead")
+    assert np.array_equal(Os[0], V[0])  # row 0 sees only key 0
+    ones = np.ones_like(V)
+    O1, _ = O.attention(Q, K, ones, kept, B, 0.5, "qhead")
+    assert np.allclose(O1, 1.0, atol=1e-14)  # softmax rows sum to 1
+    const = np.broadcast_to(np.arange(D, dtype=np.float64), V.shape).copy()
+    Oc, _ = O.attention(Q, K, const, kept, B, 0.5, "qhead")
+    assert np.allclose(Oc, const, atol=1e-13)
+
+
+def test_group_granularity_shares_rows_across_heads():
+    rng = np.random.default_rng(16)
+    S, Hq, Hkv, D, B = 32, 4, 2, 4, 8
+    Q, K, V = _rand_qkv(rng, S, Hq, Hkv, D)
+    nb = S // B
+    kept_g = [[[0, i] if i else [0] for i in range(nb)], [[i] for i in range(nb)]]
+    Og, _ = O.attention(Q, K, V, kept_g, B, 0.5, "group")
+    kept_h = [kept_g[0], kept_g[0], kept_g[1], kept_g[1]]
+    Oh, _ = O.attention(Q, K, V, kept_h, B, 0.5, "qhead")
+    assert np.array_equal(Og, Oh)
+
+
+# ---------------------------------------------------------------- needles
+
+def test_planted_needle_must_be_selected():
+    """Every key of the needle block beats every other candidate's centroid score, so by
+    bilinearity the needle's centroid score is the row maximum and top-k keeps it."""
+    rng = np.random.default_rng(17)
+    S, D, B = 128, 16, 8
+    nb = S // B
+    Q = rng.standard_normal((S, 1, D)) * 0.1
+    K = rng.standard_normal((S, 1, D)) * 0.1
+    u = rng.standard_normal(D)
+    u /= np.linalg.norm(u)
+    Q[:, 0, :] += u  # every query leans on u
+    needle = 5
+    K[needle * B:(needle + 1) * B, 0, :] = 3 * u + rng.standard_normal((B, D)) * 0.01
+    qbar, _ = O.pool_queries(Q, B, 1, "qhead")
+    kbar, _ = O.pool_keys(K, B)
+    s = O.block_scores(qbar, kbar, 1, 1, "qhead")
+    p = O.SelectParams(top_k=1, force_sink=True)
+    for i in range(needle + 2, nb):
+        # the precondition that makes selection provable
+        others = [s[0, i, j] for j in range(i) if j not in (0, needle)]
+        assert (K[needle * B:(needle + 1) * B, 0] @ qbar[0, i]).min() > max(others)
+        kept, _ = O.select_row(i, s[0, i], None, p)
+        assert needle in kept
