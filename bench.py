@@ -1,0 +1,282 @@
+"""Benchmark: one block-sparse prefill layer (pool -> score/select -> attention)
+on the 128K dual-branch workload, on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dual128k]
+
+Prints ONE JSON line.  A step is one pass of the whole hot path over the
+resident inputs; ``value`` is effective TFLOP/s = algorithmic FLOPs of the kept
+blocks / step time.  ``roofline`` describes the attention kernel (HIP events
+around each launch on the launching stream); ``cpu_baseline`` times the CPU
+oracle on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "block-sparse prefill ms/layer + effective TFLOP/s at 128k (frac of MFMA peak)"
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA, vendor figure
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, vendor figure
+
+
+def attention_flops(row_ptr, col_idx, cfg) -> float:
+    """Kept algorithmic FLOPs of one attention launch: 4*D per valid (query, key)
+    pair of every kept (row, block); B^2 pairs off the diagonal and B(B+1)/2 on
+    it (ragged last block counted exactly); times the heads a row serves."""
+    import numpy as np
+    B, S, D, nb = cfg.block_size, cfg.seq_len, cfg.head_dim, cfg.num_blocks
+    heads_per_row = cfg.group_size if cfg.granularity == "group" else 1
+    rp = np.asarray(row_ptr, dtype=np.int64)
+    ci = np.asarray(col_idx, dtype=np.int64)
+    rows = np.repeat(np.arange(len(rp) - 1), np.diff(rp))
+    i = rows % nb
+    nq = np.minimum(B, S - i * B)                # queries in block i
+    nk = np.minimum(B, S - ci * B)               # keys in block j
+    diag = ci == i
+    pairs = np.where(diag, nq * (nq + 1) // 2, nq * nk)
+    return float(4 * D * heads_per_row * pairs.sum())
+
+
+def dense_causal_flops(cfg) -> float:
+    S, D, Hq = cfg.seq_len, cfg.head_dim, cfg.num_q_heads
+    return 4.0 * D * Hq * S * (S + 1) / 2
+
+
+def pool_select_bytes(cfg, nnz: int) -> float:
+    """Algorithmic HBM bytes of pool + score/select: Q and K read once (plus E4M3
+    scales), centroids/norms/radii written and read once, CSR written."""
+    S, Hq, Hkv, D, nb, U = (cfg.seq_len, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim,
+                            cfg.num_blocks, cfg.num_units)
+    es = 1 if cfg.dtype == "fp8" else 2
+    b = S * (Hq + Hkv) * D * es
+    if cfg.dtype == "fp8":
+        b += (Hq + Hkv) * nb * 4
+    b += 2 * ((U * nb * D + Hkv * nb * D) * 4 + (U * nb + Hkv * nb) * 4)
+    b += 4 * (U * nb + 1) + 4 * nnz
+    return float(b)
+
+
+def source_hash(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "block_sparse_attention_36_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(kernel_hash: str):
+    """HBM bytes per attention launch from the committed counter summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "attention_dual128k_counters.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_hash") != kernel_hash:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, inp, sel_rows, budget_s: float = 15.0):
+    """Time the CPU oracle on a sample of the workload: for sampled selection rows,
+    pool the query block, score it against every key block of its kv head, select,
+    and run attention for the row's heads; key pooling for the touched kv heads is
+    included.  Reported as oracle TFLOP/s on the same kept-FLOP definition."""
+    import numpy as np
+    import torch
+    from oracle import bsa_oracle as O
+    B, S, D, nb = cfg.block_size, cfg.seq_len, cfg.head_dim, cfg.num_blocks
+    Hq, Hkv, G = cfg.num_q_heads, cfg.num_kv_heads, cfg.group_size
+    gran = cfg.granularity
+    p = O.SelectParams(cfg.top_k, cfg.force_sink, cfg.gate, cfg.gate_threshold, cfg.gate_factor,
+                       cfg.score_temperature, cfg.mass_threshold,
+                       cfg.rescue_fraction).as_library_precision()
+    rng = np.random.default_rng(0)
+    kv = 0
+    t_host = time.perf_counter()
+    kraw = inp.k[:, kv].cpu().view(torch.int16).numpy().view(np.uint16)
+    vraw = inp.v[:, kv].cpu().view(torch.int16).numpy().view(np.uint16)
+    copy_s = time.perf_counter() - t_host
+    t0 = time.perf_counter()
+    K = O.decode_bf16(kraw)[:, None, :]
+    V = O.decode_bf16(vraw)[:, None, :]
+    kbar, rad = O.pool_keys(K, B)
+    flops = 0.0
+    units = 0
+    heads = [h for h in range(Hq) if h // G == kv]
+    while time.perf_counter() - t0 < budget_s:
+        i = int(rng.integers(nb))
+        h = heads[int(rng.integers(len(heads)))]
+        u = h if gran == "qhead" else kv
+        q_rows = inp.q[i * B:min(S, (i + 1) * B)].cpu()
+        qh = O.decode_bf16(q_rows.view(torch.int16).numpy().view(np.uint16))
+        qbar, qn = O.pool_queries(qh, B, Hkv, gran)
+        s = qbar[u, 0] @ kbar[0, : i + 1].T
+        b = s + qn[u, 0] * rad[0, : i + 1]
+        kept, _ = O.select_row(i, s, b, p)
+        keys = O.block_tokens(kept, B, S)
+        O.attend(qh[:, h], i * B + np.arange(qh.shape[0]), K[keys, 0], V[keys, 0], keys,
+                 1 / math.sqrt(D))
+        nq = min(B, S - i * B)
+        for j in kept:
+            nk = min(B, S - j * B)
+            flops += 4 * D * (nq * (nq + 1) // 2 if j == i else nq * nk)
+        units += 1
+    el = time.perf_counter() - t0
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([x.get("num_threads", 1) for x in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        cores = len(os.sched_getaffinity(0))
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": (f"{units} random (query block, head) rows of kv head 0 at S={S}: "
+                       f"pool + score vs all key blocks + select + attention, plus pooling of "
+                       f"kv head 0's {nb} key blocks, {el:.1f} s of float64 NumPy "
+                       f"(host copy {copy_s:.1f} s excluded)"),
+            "seconds": round(el, 2)}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="dual128k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}): the block-sparse "
+              "prefill path here has no multi-GPU mode.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    import block_sparse_attention_36_amd as bsa
+    from workloads import config_by_name, generate
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    bsa.load_library()
+    cfg = config_by_name(args.workload)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] generating {cfg.name} S={cfg.seq_len} Hq={cfg.num_q_heads} "
+          f"Hkv={cfg.num_kv_heads} on the GPU", file=sys.stderr, flush=True)
+    inp = generate(cfg, dev)
+    torch.cuda.synchronize()
+
+    gran = bsa.BSA_SEL_PER_GROUP if cfg.granularity == "group" else bsa.BSA_SEL_PER_QHEAD
+    problem = bsa.make_problem(inp.q, inp.k, cfg.block_size, gran)
+    params = bsa.make_params(cfg.top_k, cfg.force_sink,
+                             bsa.BSA_GATE_TOP12_GAP if cfg.gate == "top12_gap" else bsa.BSA_GATE_NONE,
+                             cfg.gate_threshold, cfg.gate_factor, cfg.score_temperature,
+                             cfg.mass_threshold, cfg.rescue_fraction)
+    rescue = cfg.rescue_fraction > 0
+    pool = bsa.bsa_pool(problem, inp.q, inp.k, inp.q_scale, inp.k_scale, want_norm=rescue,
+                        want_radius=rescue)
+    bufs = bsa.SelectBuffers(problem, params, dev, export=False)
+    out = torch.empty(cfg.seq_len, cfg.num_q_heads, cfg.head_dim, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(cfg.num_q_heads, cfg.seq_len, dtype=torch.float32, device=dev)
+    scale = 1.0 / math.sqrt(cfg.head_dim)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        bsa.bsa_pool(problem, inp.q, inp.k, inp.q_scale, inp.k_scale, out=pool)
+        if ev:
+            ev[1].record()
+        sel = bsa.bsa_score_select(problem, params, pool, buffers=bufs)
+        if ev:
+            ev[2].record()
+        bsa.bsa_attention_fwd(problem, inp.q, inp.k, inp.v, sel.row_ptr, sel.col_idx, scale,
+                              inp.q_scale, inp.k_scale, inp.v_scale, out=out, lse=lse)
+        if ev:
+            ev[3].record()
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    rp = bufs.row_ptr.cpu().numpy()
+    nnz = int(rp[-1])
+    ci = bufs.col_idx[:nnz].cpu().numpy()
+    kept_flops = attention_flops(rp, ci, cfg)
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pool_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    sel_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    att_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
+    ms_per_step = wall * 1e3 / args.steps
+    attn_avg = float(att_ms.mean())
+    achieved = kept_flops / (attn_avg * 1e-3) / 1e12
+    ps_bytes = pool_select_bytes(cfg, nnz)
+    ps_ms = float(pool_ms.mean() + sel_ms.mean())
+    khash = source_hash("attention.hip", "common.h")
+    dense = dense_causal_flops(cfg)
+    causal_blocks = cfg.num_units * cfg.num_blocks * (cfg.num_blocks + 1) / 2
+    res = {
+        "metric": METRIC,
+        "value": round(kept_flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "fp8-e4m3 inputs, bf16 MFMA",
+        "data": "synthetic (seeded generator, random structure; no model weights)",
+        "config": {"workload": cfg.name, "seq_len": cfg.seq_len, "num_q_heads": cfg.num_q_heads,
+                   "num_kv_heads": cfg.num_kv_heads, "head_dim": cfg.head_dim,
+                   "block_size": cfg.block_size, "selection": {
+                       "top_k": cfg.top_k, "force_sink": cfg.force_sink, "gate": cfg.gate,
+                       "mass_threshold": cfg.mass_threshold,
+                       "rescue_fraction": cfg.rescue_fraction}},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic_from_profile(khash), "kernel": "attn_fwd_kernel<128,128>",
+                     "kernel_source_hash": khash},
+        "stages_ms": {"pool": round(float(pool_ms.mean()), 4),
+                      "score_select": round(float(sel_ms.mean()), 4),
+                      "attention": round(attn_avg, 4)},
+        "frac_of_bf16_peak_whole_step": round(kept_flops / (ms_per_step * 1e-3) / 1e12
+                                              / PEAK_BF16_TFLOPS, 4),
+        "kept_tflop": round(kept_flops / 1e12, 4),
+        "density": round(nnz / causal_blocks, 5),
+        "dense_causal_tflop": round(dense / 1e12, 3),
+        "pool_select": {"algorithmic_gb": round(ps_bytes / 1e9, 4),
+                        "gbs": round(ps_bytes / (ps_ms * 1e-3) / 1e9, 1),
+                        "frac_hbm": round(ps_bytes / (ps_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(cfg, inp, None, args.cpu_seconds)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

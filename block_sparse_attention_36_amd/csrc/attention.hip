@@ -1,0 +1,508 @@
+// Block-sparse attention forward on the bf16 matrix cores of CDNA4 (gfx950).
+//
+// Method: each query block attends only over the key blocks its selection row
+// kept, with the causal mask inside the diagonal block, as FlashAttention does
+// over the fused sparse mask (RBS-Attention, third paragraph; MiniMax MSA,
+// "What is MSA and how does it work": the main branch attends over the
+// preselected blocks only).  Softmax is computed online, block by block.
+//
+// Work decomposition: one workgroup of four waves per (query head, query block).
+// Wave w takes query half (w & 1) and key half (w >> 1) of every kept block, so a
+// wave owns a 64-query x 64-key tile (B = 128) and keeps its own running max, sum
+// and output; the two key halves are merged once, at the end.  The score tile is
+// computed transposed, S^T = K Q^T, so that each lane holds one query column:
+// the per-query max and sum are lane-local except for a single exchange between
+// the two 32-lane halves (V_PERMLANE32_SWAP).  The probabilities then feed the
+// second product O^T = V^T P^T straight from registers as the B operand, and the
+// V^T operand is read from the row-major V tile with the gfx950 transposing LDS
+// load (DS_READ_B64_TR_B16), so V is never transposed in memory.
+//
+// Memory: K and V tiles are double-buffered in LDS (2 x 64 KiB at D = B = 128)
+// and filled by direct global->LDS DMA one block ahead, so the next block streams
+// in while the current one is computed and no registers hold staged data.  LDS
+// rows are XOR-swizzled in 16-byte chunks so that both the 16-byte K reads (32
+// rows, one column) and the transposing V reads (4 rows, 2 chunks per 16 lanes)
+// are free of bank conflicts.  The grid is ordered by descending query block
+// (longest rows first) and maps the heads of one GQA group at one query block to
+// the same XCD, so their shared K/V blocks meet in the same L2.
+//
+// FP8 inputs (OCP E4M3): the raw codes are DMA'd, then expanded to bf16 in LDS
+// (exact); q_scale and k_scale fold into the per-block logit scale and v_scale
+// into the probabilities.
+#include "common.h"
+#include "launch.h"
+
+namespace bsa {
+
+namespace {
+
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* q_scale;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* row_ptr;
+  const int32_t* col_idx;
+  void* out;
+  float* lse;
+  int64_t S;
+  int Hq, Hkv, nb, per_group;
+  float scale_log2;
+};
+
+template <int D, int B>
+struct Cfg {
+  static constexpr int QW = B / 2;       // queries per wave
+  static constexpr int KW = B / 2;       // keys per wave per block
+  static constexpr int NQT = QW / 32;    // 32-query tiles per wave
+  static constexpr int NKT = KW / 32;    // 32-key tiles per wave
+  static constexpr int NDS = D / 16;     // contraction steps of S^T = K Q^T
+  static constexpr int NDT = D / 32;     // 32-row d tiles of O^T
+  static constexpr int NKS = KW / 16;    // contraction steps of O^T = V^T P^T
+  static constexpr int ROWB = D * 2;     // bytes per bf16 LDS row
+  static constexpr int TILE = B * ROWB;  // one bf16 K or V tile in LDS
+  static constexpr int STAGE = 2 * TILE;
+};
+
+// XOR applied to the 16-byte chunk index of LDS row r, shared by the K and V
+// tiles.  It places the 16 rows of one chunk column (the K operand reads) and
+// the 4 rows x 2 chunks of one transposing V read on distinct 16-byte slots of a
+// 256-byte bank window, so neither access pattern has bank conflicts.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  return D == 128 ? (((r & 7) << 1) | ((r >> 3) & 1)) : ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
+}
+template <int D>
+__device__ __forceinline__ int k_off(int r, int c) {
+  return r * (D * 2) + ((c ^ swz<D>(r)) << 4);
+}
+template <int D>
+__device__ __forceinline__ int v_off(int r, int c) {
+  return k_off<D>(r, c);
+}
+
+__device__ __forceinline__ s16x4 lds_read_tr16(const unsigned char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+}
+
+// ---- staging: global -> LDS by direct-to-LDS DMA (GLOBAL_LOAD_LDS_DWORDX4).
+// One DMA instruction moves 64 lanes x 16 bytes into 1 KiB of LDS at M0, lane
+// L landing at byte 16L; the swizzle is applied by choosing which global chunk
+// lane L fetches.  The loads are issued from inline asm (they have no register
+// results) so that the compiler does not serialise them against the LDS reads
+// of the other buffer; completion is awaited explicitly (s_waitcnt vmcnt) before
+// the workgroup barrier.
+
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return (unsigned)(size_t)(__attribute__((address_space(3))) const void*)p;
+}
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// 16 bytes per lane from sbase + voff (SADDR form: uniform 64-bit base in SGPRs,
+// 32-bit per-lane byte offset) into LDS at M0 + 16 * lane.
+__device__ __forceinline__ void dma16(const void* sbase, unsigned voff, unsigned lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_base), "v"(voff),
+               "s"(sbase)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier that also completes this wave's LDS accesses; the memory
+// clobber keeps the compiler from moving loads or stores across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int D, int B, bool FP8>
+struct Stage {
+  typedef Cfg<D, B> C;
+  static constexpr int RAW_TILE = FP8 ? B * D : C::TILE;  // bytes of K (or V) per block
+  static constexpr int NI = RAW_TILE / 4096;               // DMA instructions per wave per tile
+  static constexpr int NPW = 2 * NI;                       // per wave per block
+  static constexpr int RAW_STAGE = 2 * RAW_TILE;
+  // raw stages [0, 2*RAW_STAGE); FP8 adds the bf16 compute stage after them
+  static constexpr int LDS_BYTES = FP8 ? 2 * RAW_STAGE + C::STAGE : 2 * C::STAGE;
+  static_assert(NI >= 1 && RAW_TILE % 4096 == 0, "tile must split into 1 KiB DMAs per wave");
+
+  // DMA key block j of kv head g into raw stage `dst` (K tile then V tile).  K and
+  // V share the per-lane offsets; rows past the ragged end re-read the last row
+  // (their logits are masked).
+  static __device__ __forceinline__ void issue(const AttnArgs& a, int g, int j, unsigned char* dst,
+                                               int wave, int l) {
+    constexpr int ES = FP8 ? 1 : 2;                      // bytes per element
+    const unsigned rs = (unsigned)(a.Hkv * D * ES);      // bytes per token row
+    const size_t blk = ((size_t)j * B * a.Hkv + (size_t)g) * D * ES;
+    const unsigned char* kb = (const unsigned char*)a.k + blk;
+    const unsigned char* vb = (const unsigned char*)a.v + blk;
+    const int64_t left = a.S - (int64_t)j * B;
+    const int rmax = left < B ? (int)left - 1 : B - 1;
+#pragma unroll
+    for (int n = 0; n < NI; ++n) {
+      const int base = (wave * NI + n) * 1024;
+      const int p = base + 16 * l;
+      int r, col;  // tile row and byte column of this lane's 16 bytes
+      if (!FP8) {
+        r = p / C::ROWB;
+        col = (((p % C::ROWB) >> 4) ^ swz<D>(r)) << 4;
+      } else {
+        r = p / D;
+        col = p % D;
+      }
+      const unsigned off = (unsigned)(r < rmax ? r : rmax) * rs + (unsigned)col;
+      dma16(kb, off, lds_addr(dst + base));
+      dma16(vb, off, lds_addr(dst + RAW_TILE + base));
+    }
+  }
+
+  // FP8 only: expand the raw E4M3 tiles of `raw` into the swizzled bf16 stage.
+  static __device__ __forceinline__ void expand(const unsigned char* raw, unsigned char* kt,
+                                                unsigned char* vt, int tid) {
+    constexpr int NC8 = D / 16;         // 16-code chunks per row
+    constexpr int PER = B * NC8 / 256;  // chunks per thread per tile
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int n = 0; n < PER; ++n) {
+        const int ci = tid + 256 * n;
+        const int r = ci / NC8, c = ci % NC8;
+        const u32x4 w = *(const u32x4*)(raw + t * RAW_TILE + ci * 16);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const u32x2 x0 = e4m3x4_to_bf16x4(w[2 * hh]), x1 = e4m3x4_to_bf16x4(w[2 * hh + 1]);
+          const int off = t ? v_off<D>(r, 2 * c + hh) : k_off<D>(r, 2 * c + hh);
+          *(u32x4*)((t ? vt : kt) + off) = u32x4{x0[0], x0[1], x1[0], x1[1]};
+        }
+      }
+    }
+  }
+};
+
+template <int D, int B, bool FP8>
+__global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
+  typedef Cfg<D, B> C;
+  typedef Stage<D, B, FP8> ST;
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  const int tid = threadIdx.x, l = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int qh = wave & 1, kh = wave >> 1, hf = l >> 5;
+
+  // ---- (head, query block) of this workgroup: heads of one group at one query
+  // block share an XCD (workgroup id mod 8); rows go longest first.
+  const int G = a.Hq / a.Hkv, nb = a.nb;
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, t8 = bid >> 3;
+  const int hh = t8 % G;
+  const int r = (t8 / G) * 8 + xcd;
+  if (r >= a.Hkv * nb) return;  // padding workgroup (uniform: no barrier reached)
+  const int i = nb - 1 - r / a.Hkv, g = r % a.Hkv;
+  const int h = g * G + hh;
+  const int unit = a.per_group ? g : h;
+  const int row = unit * nb + i;
+  const int e0 = a.row_ptr[row], e1 = a.row_ptr[row + 1];
+  const int nblk = e1 - e0;
+  auto block_at = [&](int n) {
+    const int j = a.col_idx[e0 + n];
+    return (j >= 0 && j <= i) ? j : -1;  // -1: entry outside the causal range, skipped
+  };
+  if (nblk > 0) {
+    const int j0 = block_at(0);
+    ST::issue(a, g, j0 < 0 ? 0 : j0, lds, wave, l);
+  }
+
+  // ---- Q fragments (B operand of S^T = K Q^T): query column = lane % 32,
+  // contraction index d = ds*16 + hf*8 + [0, 8)
+  bf16x8 qf[C::NQT][C::NDS];
+  const float qsc = FP8 ? a.q_scale[(size_t)h * nb + i] : 1.0f;
+#pragma unroll
+  for (int qt = 0; qt < C::NQT; ++qt) {
+    // rows past the ragged end load the last row instead (their outputs are not stored)
+    int64_t t = (int64_t)i * B + qh * C::QW + qt * 32 + (l & 31);
+    t = t < a.S ? t : a.S - 1;
+#pragma unroll
+    for (int ds = 0; ds < C::NDS; ++ds) {
+      const size_t off = ((size_t)t * a.Hq + h) * D + ds * 16 + hf * 8;
+      if (!FP8) {
+        qf[qt][ds] = __builtin_bit_cast(bf16x8, *(const u32x4*)((const uint16_t*)a.q + off));
+      } else {
+        const u32x2 raw = *(const u32x2*)((const uint8_t*)a.q + off);
+        const u32x2 lo = e4m3x4_to_bf16x4(raw[0]), hi = e4m3x4_to_bf16x4(raw[1]);
+        qf[qt][ds] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+      }
+    }
+  }
+
+  f32x16 o[C::NDT][C::NQT];
+  float m[C::NQT], lsum[C::NQT];
+#pragma unroll
+  for (int qt = 0; qt < C::NQT; ++qt) {
+    m[qt] = -INFINITY;
+    lsum[qt] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt) o[dt][qt] = f32x16{0};
+  }
+
+  for (int n = 0; n < nblk; ++n) {
+    const int j = block_at(n);
+    unsigned char* raw = lds + (n & 1) * ST::RAW_STAGE;
+    if (n + 1 < nblk) {
+      const int jn = block_at(n + 1);
+      ST::issue(a, g, jn < 0 ? 0 : jn, lds + ((n + 1) & 1) * ST::RAW_STAGE, wave, l);
+      wait_vmcnt<ST::NPW>();  // this wave's DMAs of block n have landed
+    } else {
+      wait_vmcnt<0>();
+    }
+    lds_barrier();  // ... and every other wave's
+    unsigned char* kt = raw;
+    if (FP8) {
+      kt = lds + 2 * ST::RAW_STAGE;
+      ST::expand(raw, kt, kt + C::TILE, tid);
+      lds_barrier();
+    }
+    unsigned char* vt = kt + C::TILE;
+
+    if (j >= 0) {
+      // ---- S^T = K Q^T: A = K rows (keys), B = Q columns (queries).
+      // Row kh*KW + kt2*32 + (l&31) has the same swizzle for every kt2 (it depends
+      // on the row's low 4 bits only), so one lane address per contraction step
+      // serves both key tiles, the tile offset folding into the instruction.
+      f32x16 s[C::NKT][C::NQT];
+#pragma unroll
+      for (int kt2 = 0; kt2 < C::NKT; ++kt2)
+#pragma unroll
+        for (int qt = 0; qt < C::NQT; ++qt) s[kt2][qt] = f32x16{0};
+      const unsigned char* krow = kt + (kh * C::KW + (l & 31)) * C::ROWB;
+      const int kx = hf ^ swz<D>(l & 31);
+#pragma unroll
+      for (int ds = 0; ds < C::NDS; ++ds) {
+        const unsigned char* ka = krow + (((2 * ds) ^ kx) << 4);
+#pragma unroll
+        for (int kt2 = 0; kt2 < C::NKT; ++kt2) {
+          const bf16x8 kf = *(const bf16x8*)(ka + kt2 * 32 * C::ROWB);
+#pragma unroll
+          for (int qt = 0; qt < C::NQT; ++qt)
+            s[kt2][qt] =
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qt][ds], s[kt2][qt], 0, 0, 0);
+        }
+      }
+
+      // ---- online softmax (log2 domain); lane = one query, registers = keys.
+      // The running reference max only moves when the block max exceeds it by
+      // more than 8 (a factor 256), so the output rescale is rare; every
+      // probability stays below 2^8 and the result is the same up to rounding.
+      const float sl = a.scale_log2 * (FP8 ? qsc * a.k_scale[(size_t)g * nb + j] : 1.0f);
+      const float vsc = FP8 ? a.v_scale[(size_t)g * nb + j] : 1.0f;
+      // causal mask on the diagonal block and the ragged tail: key (kt2, v) of this
+      // lane sits at offset kw = kt2*32 + (v>>2)*8 + (v&3) from the lane's first
+      // key; it is masked when kw exceeds a per-lane limit (block-dependent, so
+      // the comparisons stay inside the loop and only run on those blocks)
+      const bool masked = (j == i) || ((int64_t)j * B + kh * C::KW + C::KW > a.S);
+      const int kfirst = kh * C::KW + hf * 4;
+      const int64_t left = a.S - (int64_t)j * B - 1 - kfirst;  // last valid kw
+#pragma unroll
+      for (int qt = 0; qt < C::NQT; ++qt) {
+        float mx = -INFINITY;
+        if (masked) {
+          const int qi = qh * C::QW + qt * 32 + (l & 31);  // query index in the block
+          int lim = (int)(left < 4 * B ? left : 4 * B);
+          if (j == i) lim = min(lim, qi - kfirst);
+#pragma unroll
+          for (int kt2 = 0; kt2 < C::NKT; ++kt2)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int kw = kt2 * 32 + (v >> 2) * 8 + (v & 3);
+              const float x = kw > lim ? -INFINITY : s[kt2][qt][v] * sl;
+              s[kt2][qt][v] = x;
+              mx = fmaxf(mx, x);
+            }
+        } else {
+#pragma unroll
+          for (int kt2 = 0; kt2 < C::NKT; ++kt2)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const float x = s[kt2][qt][v] * sl;
+              s[kt2][qt][v] = x;
+              mx = fmaxf(mx, x);
+            }
+        }
+        mx = max_with_other_half(mx);
+        const bool bump = mx > m[qt] + 8.0f;  // also true for the first finite block max
+        if (__ballot(bump)) {
+          const float mnew = bump ? mx : m[qt];
+          const float alpha = exp2f(m[qt] - mnew);  // 0 when m was -inf
+          m[qt] = mnew;
+          lsum[qt] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) o[dt][qt][v] *= alpha;
+        }
+        const float mref = m[qt] == -INFINITY ? 0.f : m[qt];
+        float ps = 0.f;
+#pragma unroll
+        for (int kt2 = 0; kt2 < C::NKT; ++kt2)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const float p = exp2f(s[kt2][qt][v] - mref);
+            ps += p;
+            s[kt2][qt][v] = p;
+          }
+        lsum[qt] += ps;
+      }
+
+      // ---- O^T += V^T P^T: A = V^T (d rows, transposing LDS read), B = P^T.
+      // Key rows of one step are k0 + 4*hf + [0,4) (elements 0..3) and the same
+      // +8 (elements 4..7); their swizzle does not depend on the step, so the
+      // step offset folds into the instruction and only the d tile and the
+      // lo/hi half select a lane address.
+      const int rlo = 4 * hf + ((l & 15) >> 2);  // row within a 16-key step
+      const int cb0 = (((l >> 4) & 1) * 16 + 4 * (l & 3)) * 2;  // byte column in a d tile
+      const unsigned char* vrow = vt + (kh * C::KW + rlo) * C::ROWB + (cb0 & 15);
+#pragma unroll
+      for (int ks = 0; ks < C::NKS; ++ks) {
+        const int kt2 = ks >> 1, sb = ks & 1;
+        bf16x8 pf[C::NQT];
+#pragma unroll
+        for (int qt = 0; qt < C::NQT; ++qt) {
+          u32x4 pk;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            pk[e] = pack_bf16x2(s[kt2][qt][8 * sb + 2 * e] * vsc,
+                                s[kt2][qt][8 * sb + 2 * e + 1] * vsc);
+          pf[qt] = __builtin_bit_cast(bf16x8, pk);
+        }
+        const int step = (kt2 * 32 + sb * 16) * C::ROWB;
+#pragma unroll
+        for (int dt = 0; dt < C::NDT; ++dt) {
+          const int c = (dt * 64 + cb0) >> 4;  // chunk of this lane's 8 bytes
+          const s16x4 lo =
+              lds_read_tr16(vrow + step + ((c ^ swz<D>(rlo)) << 4));
+          const s16x4 hi =
+              lds_read_tr16(vrow + 8 * C::ROWB + step + ((c ^ swz<D>(rlo + 8)) << 4));
+          const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+          const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{lo2[0], lo2[1], hi2[0], hi2[1]});
+#pragma unroll
+          for (int qt = 0; qt < C::NQT; ++qt)
+            o[dt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qt], o[dt][qt], 0, 0, 0);
+        }
+      }
+    }
+    lds_barrier();  // every wave is done with this stage before it is refilled
+  }
+
+  // ---- merge the two key halves: lanes first (sum of the halves' partial sums),
+  // then waves kh = 1 hand their state to kh = 0 through LDS
+#pragma unroll
+  for (int qt = 0; qt < C::NQT; ++qt) lsum[qt] += other_half(lsum[qt]);
+  float* xo = (float*)lds + (size_t)qh * (C::NDT * C::NQT * 16 * 64 + 2 * C::NQT * 64);
+  float* xm = xo + C::NDT * C::NQT * 16 * 64;
+  float* xl = xm + C::NQT * 64;
+  if (kh == 1) {
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+      for (int qt = 0; qt < C::NQT; ++qt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) xo[((dt * C::NQT + qt) * 16 + v) * 64 + l] = o[dt][qt][v];
+#pragma unroll
+    for (int qt = 0; qt < C::NQT; ++qt) {
+      xm[qt * 64 + l] = m[qt];
+      xl[qt * 64 + l] = lsum[qt];
+    }
+  }
+  lds_barrier();
+  if (kh == 1) return;
+
+  uint16_t* out = (uint16_t*)a.out;
+#pragma unroll
+  for (int qt = 0; qt < C::NQT; ++qt) {
+    const float m1 = xm[qt * 64 + l], l1 = xl[qt * 64 + l];
+    const float mt = fmaxf(m[qt], m1);
+    const float mref = mt == -INFINITY ? 0.f : mt;
+    const float a0 = exp2f(m[qt] - mref), a1 = exp2f(m1 - mref);
+    const float lt = lsum[qt] * a0 + l1 * a1;
+    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+    const int qi = qh * C::QW + qt * 32 + (l & 31);
+    const int64_t t = (int64_t)i * B + qi;
+    if (t < a.S) {
+      uint16_t* orow = out + ((size_t)t * a.Hq + h) * D;
+#pragma unroll
+      for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+        for (int vg = 0; vg < 4; ++vg) {
+          float y[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int v = vg * 4 + e;
+            y[e] = (o[dt][qt][v] * a0 + xo[((dt * C::NQT + qt) * 16 + v) * 64 + l] * a1) * inv;
+          }
+          const int d = dt * 32 + vg * 8 + hf * 4;
+          *(u32x2*)(orow + d) = u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+        }
+      if (a.lse && hf == 0)
+        a.lse[(size_t)h * a.S + t] = lt > 0.f ? (mt + log2f(lt)) * kLn2 : -INFINITY;
+    }
+  }
+}
+
+template <int D, int B, bool FP8>
+hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
+  typedef Stage<D, B, FP8> ST;
+  const int G = a.Hq / a.Hkv;
+  const int rows8 = (a.Hkv * a.nb + 7) / 8;
+  static_assert(ST::LDS_BYTES <= 160 * 1024, "LDS budget");
+  static bool attr_set = false;
+  if (!attr_set) {
+    (void)hipFuncSetAttribute((const void*)attn_fwd_kernel<D, B, FP8>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, ST::LDS_BYTES);
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((attn_fwd_kernel<D, B, FP8>), dim3(rows8 * 8 * G), dim3(256), ST::LDS_BYTES,
+                     stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attention(const Shape& sh, const void* q, const void* k, const void* v,
+                            const float* q_scale, const float* k_scale, const float* v_scale,
+                            const int32_t* row_ptr, const int32_t* col_idx, float softmax_scale,
+                            void* out, float* lse, hipStream_t stream) {
+  AttnArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.q_scale = q_scale;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.row_ptr = row_ptr;
+  a.col_idx = col_idx;
+  a.out = out;
+  a.lse = lse;
+  a.S = sh.S;
+  a.Hq = sh.Hq;
+  a.Hkv = sh.Hkv;
+  a.nb = sh.nb;
+  a.per_group = sh.per_group;
+  a.scale_log2 = softmax_scale * kLog2e;
+#define BSA_ATTN(DD, BB) \
+  if (sh.D == DD && sh.B == BB) \
+    return sh.fp8 ? launch_t<DD, BB, true>(a, stream) : launch_t<DD, BB, false>(a, stream);
+  BSA_ATTN(128, 128)
+  BSA_ATTN(128, 64)
+  BSA_ATTN(64, 64)
+  BSA_ATTN(64, 128)
+#undef BSA_ATTN
+  return hipErrorInvalidValue;
+}
+
+}  // namespace bsa

@@ -1,0 +1,97 @@
+// Device-side helpers shared by the HIP kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsa {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// Value held by lane (l ^ 32): V_PERMLANE32_SWAP exchanges the upper half of the
+// first operand with the lower half of the second; swapping x with itself leaves
+// {x[l], x[l+32]} in lanes l < 32 and {x[l-32], x[l]} in lanes l >= 32.
+__device__ __forceinline__ float other_half(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(threadIdx.x & 32 ? r[0] : r[1]);
+}
+
+__device__ __forceinline__ float max_with_other_half(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Round-to-nearest-even float -> bf16 bits (inputs here are finite).
+__device__ __forceinline__ unsigned short f32_to_bf16_bits(float f) {
+  unsigned u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (unsigned short)(u >> 16);
+}
+
+__device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
+  return (unsigned)f32_to_bf16_bits(lo) | ((unsigned)f32_to_bf16_bits(hi) << 16);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(unsigned short b) {
+  return __uint_as_float((unsigned)b << 16);
+}
+
+// OCP E4M3 decoding with the gfx950 conversion instructions (exact for every
+// code: E4M3 values are representable in both bf16 and fp32).
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+
+// Four E4M3 codes (one dword) -> four bf16 packed in two dwords.
+__device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(unsigned w) {
+  const bf16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+  const bf16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+  return u32x2{__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi)};
+}
+
+// Four E4M3 codes (one dword) -> four floats.
+__device__ __forceinline__ f32x4 e4m3x4_to_f32x4(unsigned w) {
+  const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+  const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+  return f32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+// Order-preserving map float -> uint32 (larger float, larger key; -0 < +0).
+__device__ __forceinline__ unsigned float_key(float f) {
+  unsigned u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+  // fixed butterfly: the same tree on every call, so results are reproducible
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
+__device__ __forceinline__ int wave_sum_int(int x) {
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+__device__ __forceinline__ unsigned long long ballot64(bool p) { return __ballot(p); }
+
+__device__ __forceinline__ unsigned long long lanemask_lt() {
+  const int l = lane_id();
+  return l ? (~0ull >> (64 - l)) : 0ull;
+}
+
+}  // namespace bsa

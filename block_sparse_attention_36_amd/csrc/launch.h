@@ -1,0 +1,46 @@
+// Internal host-side interface between the C ABI (api.cpp) and the kernels.
+// Every launcher assumes its arguments were validated by api.cpp and only
+// enqueues work on the given stream; it returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace bsa {
+
+struct Shape {
+  int64_t S;
+  int Hq, Hkv, D, B, nb, fp8, per_group;
+  int G() const { return Hq / Hkv; }
+  int U() const { return per_group ? Hkv : Hq; }
+};
+
+hipError_t launch_pool(const Shape& sh, const void* q, const void* k, const float* q_scale,
+                       const float* k_scale, float* q_centroid, float* q_norm, float* k_centroid,
+                       float* k_radius, hipStream_t stream);
+
+struct SelectConfig {
+  int top_k, force_sink, gate, gate_factor;
+  float gate_threshold, temperature, mass_threshold;
+  double rescue_fraction;
+};
+
+// Workspace carve-up used by launch_score_select (byte offsets, 256-aligned).
+struct SelectWorkspace {
+  size_t scores_off, mask_off, counts_off, total;
+};
+SelectWorkspace select_workspace_layout(const Shape& sh, bool export_scores);
+
+hipError_t launch_score_select(const Shape& sh, const SelectConfig& cfg, const float* q_centroid,
+                               const float* q_norm, const float* k_centroid,
+                               const float* k_radius, int32_t* row_ptr, int32_t* col_idx,
+                               int64_t col_capacity, float* scores_out, float* bound_out,
+                               uint8_t* gate_out, void* workspace, hipStream_t stream);
+
+hipError_t launch_attention(const Shape& sh, const void* q, const void* k, const void* v,
+                            const float* q_scale, const float* k_scale, const float* v_scale,
+                            const int32_t* row_ptr, const int32_t* col_idx, float softmax_scale,
+                            void* out, float* lse, hipStream_t stream);
+
+}  // namespace bsa

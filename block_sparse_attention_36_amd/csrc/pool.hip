@@ -1,0 +1,250 @@
+// Block pooling: query/key block centroids, query-centroid norms, key-block radii.
+//
+// Method: keys are grouped into blocks of B tokens and each block is represented
+// by its mean ("Uncertainty-gated selection for block-sparse attention", technical
+// summary, Methodology step 1: mean-pooling backbone); the rescue branch needs a
+// per-(prompt, layer, head) key-block radius (RBS-Attention, third and fourth
+// paragraphs), here the largest distance of a key from its block mean.
+//
+// Design: HBM-bound streaming reduction.  One workgroup per (token block, chunk of
+// heads); each thread owns 8 consecutive elements of the [H*D] token row, so every
+// row load is one contiguous, fully coalesced 16-byte (bf16) or 8-byte (E4M3)
+// access per thread, and the reduction over the block's rows stays in registers.
+// Rows are loaded eight at a time to keep enough bytes in flight per thread.
+#include "common.h"
+#include "launch.h"
+
+namespace bsa {
+
+namespace {
+
+template <bool FP8>
+struct RowLoad;
+
+template <>
+struct RowLoad<false> {  // 8 bf16
+  typedef u32x4 raw;
+  static __device__ __forceinline__ raw load(const void* p) { return *(const u32x4*)p; }
+  static __device__ __forceinline__ void add(float* acc, const raw& v) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[2 * e] += __uint_as_float(v[e] << 16);
+      acc[2 * e + 1] += __uint_as_float(v[e] & 0xFFFF0000u);
+    }
+  }
+  static __device__ __forceinline__ void decode(float* x, const raw& v) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = __uint_as_float(v[e] << 16);
+      x[2 * e + 1] = __uint_as_float(v[e] & 0xFFFF0000u);
+    }
+  }
+  static constexpr int elem_bytes = 2;
+};
+
+template <>
+struct RowLoad<true> {  // 8 E4M3 codes
+  typedef u32x2 raw;
+  static __device__ __forceinline__ raw load(const void* p) { return *(const u32x2*)p; }
+  static __device__ __forceinline__ void decode(float* x, const raw& v) {
+    const f32x4 a = e4m3x4_to_f32x4(v[0]), b = e4m3x4_to_f32x4(v[1]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[e] = a[e];
+      x[4 + e] = b[e];
+    }
+  }
+  static __device__ __forceinline__ void add(float* acc, const raw& v) {
+    float x[8];
+    decode(x, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += x[e];
+  }
+  static constexpr int elem_bytes = 1;
+};
+
+// Sum of `cnt` rows (stride row_stride elements) of 8 consecutive elements at base.
+template <bool FP8>
+__device__ __forceinline__ void sum_rows(const unsigned char* base, size_t row_bytes, int cnt,
+                                         float* acc) {
+  typedef RowLoad<FP8> L;
+  int t = 0;
+  for (; t + 8 <= cnt; t += 8) {
+    typename L::raw v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = L::load(base + (size_t)(t + u) * row_bytes);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) L::add(acc, v[u]);
+  }
+  for (; t < cnt; ++t) L::add(acc, L::load(base + (size_t)t * row_bytes));
+}
+
+// Sum over the D/8 consecutive lanes that hold one head's row.
+template <int D>
+__device__ __forceinline__ float head_lane_sum(float x) {
+#pragma unroll
+  for (int o = D / 16; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+template <bool FP8, int D>
+__global__ void pool_q_kernel(const void* __restrict__ q, const float* __restrict__ q_scale,
+                              float* __restrict__ qc, float* __restrict__ qn, int64_t S, int Hq,
+                              int Hkv, int B, int nb, int per_group, int HW) {
+  extern __shared__ float red[];  // [HW][D], per-head means for the group sum
+  typedef RowLoad<FP8> L;
+  const int i = blockIdx.x;
+  const int h0 = blockIdx.y * HW;
+  const int tid = threadIdx.x;
+  const int hl = (tid * 8) / D, d = (tid * 8) % D;
+  const int h = h0 + hl;
+  const bool active = h < Hq;
+  const int64_t t0 = (int64_t)i * B;
+  const int cnt = (int)((S - t0) < B ? (S - t0) : B);
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (active) {
+    const size_t row_bytes = (size_t)Hq * D * L::elem_bytes;
+    const unsigned char* base = (const unsigned char*)q + (size_t)t0 * row_bytes +
+                                ((size_t)h * D + d) * L::elem_bytes;
+    sum_rows<FP8>(base, row_bytes, cnt, acc);
+  }
+  const float mul = (FP8 && active ? q_scale[(size_t)h * nb + i] : 1.0f) / (float)cnt;
+  float mean[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) mean[e] = acc[e] * mul;
+
+  if (!per_group) {
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss += mean[e] * mean[e];
+    ss = head_lane_sum<D>(ss);
+    if (active) {
+      float* dst = qc + ((size_t)h * nb + i) * D + d;
+      *(f32x4*)dst = f32x4{mean[0], mean[1], mean[2], mean[3]};
+      *(f32x4*)(dst + 4) = f32x4{mean[4], mean[5], mean[6], mean[7]};
+      if (qn && d == 0) qn[(size_t)h * nb + i] = sqrtf(ss);
+    }
+    return;
+  }
+  // per-group rows: mean over the group's heads of the per-head means
+  const int G = Hq / Hkv;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[hl * D + d + e] = mean[e];
+  __syncthreads();
+  const int ul = hl;  // this thread now works for local unit ul (if any)
+  const int u = h0 / G + ul;
+  const bool uact = ul < HW / G && u < Hkv;
+  float gm[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (uact) {
+    for (int gg = 0; gg < G; ++gg) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) gm[e] += red[(ul * G + gg) * D + d + e];
+    }
+  }
+  const float invg = 1.0f / (float)G;
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    gm[e] *= invg;
+    ss += gm[e] * gm[e];
+  }
+  ss = head_lane_sum<D>(ss);
+  if (uact) {
+    float* dst = qc + ((size_t)u * nb + i) * D + d;
+    *(f32x4*)dst = f32x4{gm[0], gm[1], gm[2], gm[3]};
+    *(f32x4*)(dst + 4) = f32x4{gm[4], gm[5], gm[6], gm[7]};
+    if (qn && d == 0) qn[(size_t)u * nb + i] = sqrtf(ss);
+  }
+}
+
+template <bool FP8, int D>
+__global__ void pool_k_kernel(const void* __restrict__ k, const float* __restrict__ k_scale,
+                              float* __restrict__ kc, float* __restrict__ kr, int64_t S, int Hkv,
+                              int B, int nb, int HW) {
+  typedef RowLoad<FP8> L;
+  const int j = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int gl = (tid * 8) / D, d = (tid * 8) % D;
+  const int g = blockIdx.y * HW + gl;
+  const bool active = g < Hkv;
+  const int64_t t0 = (int64_t)j * B;
+  const int cnt = (int)((S - t0) < B ? (S - t0) : B);
+  const size_t row_bytes = (size_t)Hkv * D * L::elem_bytes;
+  const unsigned char* base =
+      (const unsigned char*)k + (size_t)t0 * row_bytes + ((size_t)(active ? g : 0) * D + d) * L::elem_bytes;
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (active) sum_rows<FP8>(base, row_bytes, cnt, acc);
+  const float scale = (FP8 && active) ? k_scale[(size_t)g * nb + j] : 1.0f;
+  const float mul = scale / (float)cnt;
+  float c[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) c[e] = acc[e] * mul;
+  if (active) {
+    float* dst = kc + ((size_t)g * nb + j) * D + d;
+    *(f32x4*)dst = f32x4{c[0], c[1], c[2], c[3]};
+    *(f32x4*)(dst + 4) = f32x4{c[4], c[5], c[6], c[7]};
+  }
+  if (!kr) return;
+  // second pass over the (now cache-resident) block: largest distance from the mean
+  float mx = 0.f;
+  for (int t = 0; t < cnt; t += 4) {
+    typename L::raw v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (active && t + u < cnt) v[u] = L::load(base + (size_t)(t + u) * row_bytes);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      float part = 0.f;
+      if (active && t + u < cnt) {
+        float x[8];
+        L::decode(x, v[u]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float df = x[e] * scale - c[e];
+          part += df * df;
+        }
+      }
+      part = head_lane_sum<D>(part);
+      if (t + u < cnt) mx = fmaxf(mx, part);
+    }
+  }
+  if (active && d == 0) kr[(size_t)g * nb + j] = sqrtf(mx);
+}
+
+template <bool FP8, int D>
+hipError_t launch_pool_t(const Shape& sh, const void* q, const void* k, const float* q_scale,
+                         const float* k_scale, float* q_centroid, float* q_norm,
+                         float* k_centroid, float* k_radius, hipStream_t stream) {
+  const int maxh = 2048 / D;  // heads per workgroup at 256 threads
+  int HW = sh.Hq < maxh ? sh.Hq : maxh;
+  if (sh.per_group) HW = (HW / sh.G()) * sh.G();  // whole groups per workgroup
+  dim3 gq(sh.nb, (sh.Hq + HW - 1) / HW);
+  hipLaunchKernelGGL((pool_q_kernel<FP8, D>), gq, dim3(HW * D / 8), HW * D * sizeof(float), stream,
+                     q, q_scale, q_centroid, q_norm, sh.S, sh.Hq, sh.Hkv, sh.B, sh.nb,
+                     sh.per_group, HW);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int HWK = sh.Hkv < maxh ? sh.Hkv : maxh;
+  dim3 gk(sh.nb, (sh.Hkv + HWK - 1) / HWK);
+  hipLaunchKernelGGL((pool_k_kernel<FP8, D>), gk, dim3(HWK * D / 8), 0, stream, k, k_scale,
+                     k_centroid, k_radius, sh.S, sh.Hkv, sh.B, sh.nb, HWK);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_pool(const Shape& sh, const void* q, const void* k, const float* q_scale,
+                       const float* k_scale, float* q_centroid, float* q_norm, float* k_centroid,
+                       float* k_radius, hipStream_t stream) {
+  if (sh.D == 128)
+    return sh.fp8 ? launch_pool_t<true, 128>(sh, q, k, q_scale, k_scale, q_centroid, q_norm,
+                                             k_centroid, k_radius, stream)
+                  : launch_pool_t<false, 128>(sh, q, k, q_scale, k_scale, q_centroid, q_norm,
+                                              k_centroid, k_radius, stream);
+  return sh.fp8 ? launch_pool_t<true, 64>(sh, q, k, q_scale, k_scale, q_centroid, q_norm,
+                                          k_centroid, k_radius, stream)
+                : launch_pool_t<false, 64>(sh, q, k, q_scale, k_scale, q_centroid, q_norm,
+                                           k_centroid, k_radius, stream);
+}
+
+}  // namespace bsa

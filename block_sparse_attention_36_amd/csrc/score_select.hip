@@ -1,0 +1,417 @@
+// Block scores, per-row selection, and CSR emission.
+//
+// Scores: s[u][i][j] = qbar[u][i] . kbar[kv(u)][j], j <= i, the mean-pooling inner
+// product ("Uncertainty-gated selection for block-sparse attention", technical
+// summary, Methodology step 1).  Computed on the fp32 matrix cores
+// (V_MFMA_F32_32X32X2_F32), one wave per 32x32 tile of the causal lower triangle,
+// so the scores keep full fp32 accuracy.
+//
+// Selection (one wave per row (u, i)), on the candidates C_i = {0..i} minus the
+// forced blocks, ranked by descending score with the lowest index first on ties:
+//   top-k  : the first k (same page, Methodology step 2, the kv_idx list), or the
+//            first rho*k when the gate fires: p(0) - p(1) < theta for
+//            p = softmax(tau*s) over C_i (same page, lay summary "The Solution";
+//            Methodology step 5 names rho);
+//   base   : the shortest prefix whose softmax mass reaches mu (RBS-Attention, third
+//            paragraph, the base branch with its own threshold);
+//   rescue : the first ceil(phi*|C_i|) ranked by b = s + ||qbar||*r (RBS-Attention,
+//            third and fourth paragraphs, the radius rescue branch);
+//   kept   : forced U top-k U base U rescue (the masks are unioned).
+// Each branch is reduced to a threshold key T (the rank-k key, found by bisection
+// on the order-preserving integer image of the fp32 value) plus a count of
+// threshold ties admitted in index order.  All sums use a fixed reduction tree, so
+// a row's result is reproducible run to run.
+//
+// CSR: a single-workgroup exclusive scan of the row counts, then one wave per row
+// writes the set bits of its mask in ascending order.
+#include "common.h"
+#include "launch.h"
+
+namespace bsa {
+
+namespace {
+
+// ------------------------------------------------------------------ scores
+
+__global__ __launch_bounds__(64) void score_kernel(const float* __restrict__ qc,
+                                                   const float* __restrict__ kc,
+                                                   float* __restrict__ scores, int nb, int D,
+                                                   int G, int per_group) {
+  const int it = blockIdx.x, jt = blockIdx.y, u = blockIdx.z;
+  if (jt > it) return;
+  const int l = threadIdx.x;
+  const int hf = l >> 5;
+  const int g = per_group ? u : u / G;
+  const int ia = it * 32 + (l & 31), jb = jt * 32 + (l & 31);
+  const float* arow = qc + ((size_t)u * nb + (ia < nb ? ia : nb - 1)) * D + hf * (D / 2);
+  const float* brow = kc + ((size_t)g * nb + (jb < nb ? jb : nb - 1)) * D + hf * (D / 2);
+  f32x16 acc = {0};
+  // lane half hf contracts over d in [hf*D/2, (hf+1)*D/2): any split of the
+  // contraction index is valid as long as A and B use the same one
+  for (int k0 = 0; k0 < D / 2; k0 += 4) {
+    const f32x4 av = *(const f32x4*)(arow + k0);
+    const f32x4 bv = *(const f32x4*)(brow + k0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[e], bv[e], acc, 0, 0, 0);
+  }
+  const int j = jt * 32 + (l & 31);
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int i = it * 32 + (v >> 2) * 8 + hf * 4 + (v & 3);
+    if (i < nb && j <= i) scores[((size_t)u * nb + i) * nb + j] = acc[v];
+  }
+}
+
+// ------------------------------------------------------------------ selection
+
+struct SelArgs {
+  const float* scores;
+  const float* qn;
+  const float* kr;
+  float* bound_out;
+  uint8_t* gate_out;
+  unsigned long long* mask;
+  int* counts;
+  int nb, nw, rows, G, per_group;
+  int top_k, force_sink, gate, gate_factor;
+  float gate_threshold, tau_log2e, mass_threshold;
+  double rescue_fraction;
+  int use_b, use_p, per_wave_floats;
+};
+
+__device__ __forceinline__ bool is_cand(int j, int i, int sink) {
+  return j < i && !(sink && j == 0);
+}
+
+// number of candidates whose key(vals[j]) >= X
+__device__ int count_ge(const float* vals, int nslots, int i, int sink, unsigned X) {
+  const int l = lane_id();
+  int c = 0;
+  for (int e = 0; e < nslots; ++e) {
+    const int j = e * 64 + l;
+    c += (is_cand(j, i, sink) && float_key(vals[j]) >= X) ? 1 : 0;
+  }
+  return wave_sum_int(c);
+}
+
+// Threshold of the top-k over candidates: (T, need) such that the kept set is
+// {key > T} plus the first `need` candidates with key == T in index order.
+__device__ void topk_threshold(const float* vals, int nslots, int i, int sink, int nc, int k,
+                               unsigned& T, int& need) {
+  if (k >= nc) {  // every candidate
+    T = 0u;
+    need = nc;
+    return;
+  }
+  if (k <= 0) {
+    T = 0xFFFFFFFFu;
+    need = 0;
+    return;
+  }
+  unsigned t = 0u;
+  for (int bit = 31; bit >= 0; --bit) {
+    const unsigned x = t | (1u << bit);
+    if (count_ge(vals, nslots, i, sink, x) >= k) t = x;
+  }
+  const int gt = (t == 0xFFFFFFFFu) ? 0 : count_ge(vals, nslots, i, sink, t + 1u);
+  T = t;
+  need = k - gt;
+}
+
+// mass of candidates with key(s) >= X (fixed-order sum)
+__device__ float mass_ge(const float* s, const float* p, int nslots, int i, int sink, unsigned X) {
+  const int l = lane_id();
+  float m = 0.f;
+  for (int e = 0; e < nslots; ++e) {
+    const int j = e * 64 + l;
+    if (is_cand(j, i, sink) && float_key(s[j]) >= X) m += p[j];
+  }
+  return wave_sum(m);
+}
+
+__global__ __launch_bounds__(256) void select_kernel(SelArgs a) {
+  extern __shared__ float sm[];
+  const int l = lane_id();
+  const int wave = threadIdx.x >> 6;
+  const int row = blockIdx.x * (blockDim.x >> 6) + wave;
+  if (row >= a.rows) return;  // no workgroup barriers below
+  const int nb = a.nb;
+  const int u = row / nb, i = row % nb;
+  const int g = a.per_group ? u : u / a.G;
+  float* s = sm + (size_t)wave * a.per_wave_floats;
+  float* b = s + a.nw * 64;
+  float* p = b + (a.use_b ? a.nw * 64 : 0);
+  const int nslots = i / 64 + 1;
+  const int sink = a.force_sink;
+  const int nc = i > 0 ? i - (sink ? 1 : 0) : 0;
+  const float* srow = a.scores + ((size_t)u * nb + i) * nb;
+  const float qnv = a.use_b ? a.qn[(size_t)u * nb + i] : 0.f;
+  for (int e = 0; e < nslots; ++e) {
+    const int j = e * 64 + l;
+    if (j <= i) {
+      const float sv = srow[j];
+      s[j] = sv;
+      if (a.use_b) {
+        const float bv = fmaf(qnv, a.kr[(size_t)g * nb + j], sv);
+        b[j] = bv;
+        if (a.bound_out) a.bound_out[((size_t)u * nb + i) * nb + j] = bv;
+      }
+    }
+  }
+  // (each lane reads back only the entries it wrote, so no barrier is needed)
+
+  // softmax statistics over the candidates (gate and mass)
+  float s0 = -INFINITY, zsum = 0.f;
+  const bool need_soft = (a.gate && a.top_k > 0) || a.use_p;
+  if (need_soft && nc > 0) {
+    float mx = -INFINITY;
+    for (int e = 0; e < nslots; ++e) {
+      const int j = e * 64 + l;
+      if (is_cand(j, i, sink)) mx = fmaxf(mx, s[j]);
+    }
+    s0 = wave_max(mx);
+    float z = 0.f;
+    for (int e = 0; e < nslots; ++e) {
+      const int j = e * 64 + l;
+      if (is_cand(j, i, sink)) {
+        const float w = exp2f((s[j] - s0) * a.tau_log2e);
+        z += w;
+        if (a.use_p) p[j] = w;
+      }
+    }
+    zsum = wave_sum(z);
+    if (a.use_p) {
+      const float inv = 1.0f / zsum;
+      for (int e = 0; e < nslots; ++e) {
+        const int j = e * 64 + l;
+        if (is_cand(j, i, sink)) p[j] *= inv;
+      }
+    }
+  }
+
+  // top-k branch (with the optional gate)
+  unsigned Tk = 0xFFFFFFFFu;
+  int needk = 0;
+  bool fired = false;
+  if (a.top_k > 0) {
+    if (a.gate && nc >= 2) {
+      // runner-up: best candidate other than the first (lowest-index) maximum
+      int jmax = 0x7FFFFFFF;
+      for (int e = 0; e < nslots; ++e) {
+        const int j = e * 64 + l;
+        if (is_cand(j, i, sink) && s[j] == s0) jmax = min(jmax, j);
+      }
+      for (int o = 32; o >= 1; o >>= 1) jmax = min(jmax, __shfl_xor(jmax, o));
+      float m2 = -INFINITY;
+      for (int e = 0; e < nslots; ++e) {
+        const int j = e * 64 + l;
+        if (is_cand(j, i, sink) && j != jmax) m2 = fmaxf(m2, s[j]);
+      }
+      const float s1 = wave_max(m2);
+      const float gap = (1.0f - exp2f((s1 - s0) * a.tau_log2e)) / zsum;
+      fired = gap < a.gate_threshold;
+    }
+    const int keff = a.top_k * (fired ? a.gate_factor : 1);
+    topk_threshold(s, nslots, i, sink, nc, keff, Tk, needk);
+  }
+
+  // base branch: shortest prefix of the order reaching mass mu
+  unsigned Tm = 0xFFFFFFFFu;
+  int needm = 0;
+  if (a.use_p && nc > 0) {
+    unsigned t = 0u;
+    for (int bit = 31; bit >= 0; --bit) {
+      const unsigned x = t | (1u << bit);
+      if (mass_ge(s, p, nslots, i, sink, x) >= a.mass_threshold) t = x;
+    }
+    if (mass_ge(s, p, nslots, i, sink, t) < a.mass_threshold) {
+      Tm = 0u;  // the total falls short in float32: keep every candidate
+      needm = nc;
+    } else {
+      Tm = t;
+      float cum = (t == 0xFFFFFFFFu) ? 0.f : mass_ge(s, p, nslots, i, sink, t + 1u);
+      // admit ties at T in index order until the mass is reached
+      for (int e = 0; e < nslots && cum < a.mass_threshold; ++e) {
+        const int j = e * 64 + l;
+        unsigned long long tie = ballot64(is_cand(j, i, sink) && float_key(s[j]) == t);
+        while (tie && cum < a.mass_threshold) {
+          const int src = __builtin_ctzll(tie);
+          cum += __shfl(p[e * 64 + l], src);
+          ++needm;
+          tie &= tie - 1;
+        }
+      }
+    }
+  }
+
+  // rescue branch: top ceil(phi*|C_i|) by the bound
+  unsigned Tr = 0xFFFFFFFFu;
+  int needr = 0;
+  if (a.use_b && nc > 0) {
+    int nr = (int)ceil(a.rescue_fraction * (double)nc);
+    nr = nr < nc ? nr : nc;
+    topk_threshold(b, nslots, i, sink, nc, nr, Tr, needr);
+  }
+
+  // union and mask emission
+  int runk = 0, runm = 0, runr = 0, count = 0;
+  const unsigned long long lt = lanemask_lt();
+  unsigned long long* mrow = a.mask + (size_t)row * a.nw;
+  for (int e = 0; e < nslots; ++e) {
+    const int j = e * 64 + l;
+    const bool c = is_cand(j, i, sink);
+    bool keep = (j == i) || (sink && j == 0 && j <= i);
+    if (a.top_k > 0) {
+      const unsigned key = c ? float_key(s[j]) : 0u;
+      const unsigned long long tie = ballot64(c && key == Tk);
+      keep |= c && (key > Tk || ((tie >> l) & 1ull && runk + __popcll(tie & lt) < needk));
+      runk += __popcll(tie);
+    }
+    if (a.use_p) {
+      const unsigned key = c ? float_key(s[j]) : 0u;
+      const unsigned long long tie = ballot64(c && key == Tm);
+      keep |= c && (key > Tm || ((tie >> l) & 1ull && runm + __popcll(tie & lt) < needm));
+      runm += __popcll(tie);
+    }
+    if (a.use_b) {
+      const unsigned key = c ? float_key(b[j]) : 0u;
+      const unsigned long long tie = ballot64(c && key == Tr);
+      keep |= c && (key > Tr || ((tie >> l) & 1ull && runr + __popcll(tie & lt) < needr));
+      runr += __popcll(tie);
+    }
+    const unsigned long long word = ballot64(keep && j <= i);
+    if (l == 0) mrow[e] = word;
+    count += __popcll(word);
+  }
+  if (l == 0) {
+    a.counts[row] = count;
+    if (a.gate_out) a.gate_out[row] = fired ? 1 : 0;
+  }
+}
+
+// ------------------------------------------------------------------ CSR
+
+__global__ __launch_bounds__(1024) void scan_kernel(const int* __restrict__ counts,
+                                                    int32_t* __restrict__ row_ptr, int rows) {
+  __shared__ int part[1024];
+  const int t = threadIdx.x;
+  const int chunk = (rows + 1023) / 1024;
+  const int r0 = t * chunk, r1 = min(rows, r0 + chunk);
+  int sum = 0;
+  for (int r = r0; r < r1; ++r) sum += counts[r];
+  part[t] = sum;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int v = t >= o ? part[t - o] : 0;
+    __syncthreads();
+    part[t] += v;
+    __syncthreads();
+  }
+  int run = part[t] - sum;  // exclusive prefix
+  for (int r = r0; r < r1; ++r) {
+    row_ptr[r] = run;
+    run += counts[r];
+  }
+  if (t == 1023) row_ptr[rows] = part[1023];
+}
+
+__global__ __launch_bounds__(256) void compact_kernel(const unsigned long long* __restrict__ mask,
+                                                      const int32_t* __restrict__ row_ptr,
+                                                      int32_t* __restrict__ col_idx, int rows,
+                                                      int nb, int nw, int64_t capacity) {
+  const int l = lane_id();
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int i = row % nb;
+  const int nslots = i / 64 + 1;
+  const int64_t base = row_ptr[row];
+  int run = 0;
+  const unsigned long long lt = lanemask_lt();
+  for (int e = 0; e < nslots; ++e) {
+    const unsigned long long w = mask[(size_t)row * nw + e];
+    if ((w >> l) & 1ull) {
+      const int64_t pos = base + run + __popcll(w & lt);
+      if (pos < capacity) col_idx[pos] = e * 64 + l;
+    }
+    run += __popcll(w);
+  }
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+SelectWorkspace select_workspace_layout(const Shape& sh, bool export_scores) {
+  SelectWorkspace w;
+  const size_t rows = (size_t)sh.U() * sh.nb;
+  const size_t nw = (size_t)(sh.nb + 63) / 64;
+  size_t off = 0;
+  w.scores_off = off;
+  if (!export_scores) off += align256(rows * sh.nb * sizeof(float));
+  w.mask_off = off;
+  off += align256(rows * nw * sizeof(unsigned long long));
+  w.counts_off = off;
+  off += align256(rows * sizeof(int));
+  w.total = off;
+  return w;
+}
+
+hipError_t launch_score_select(const Shape& sh, const SelectConfig& cfg, const float* q_centroid,
+                               const float* q_norm, const float* k_centroid,
+                               const float* k_radius, int32_t* row_ptr, int32_t* col_idx,
+                               int64_t col_capacity, float* scores_out, float* bound_out,
+                               uint8_t* gate_out, void* workspace, hipStream_t stream) {
+  const SelectWorkspace w = select_workspace_layout(sh, scores_out != nullptr);
+  unsigned char* ws = (unsigned char*)workspace;
+  float* scores = scores_out ? scores_out : (float*)(ws + w.scores_off);
+  unsigned long long* mask = (unsigned long long*)(ws + w.mask_off);
+  int* counts = (int*)(ws + w.counts_off);
+  const int nb = sh.nb, U = sh.U(), rows = U * nb, nw = (nb + 63) / 64;
+  const int NT = (nb + 31) / 32;
+
+  hipLaunchKernelGGL(score_kernel, dim3(NT, NT, U), dim3(64), 0, stream, q_centroid, k_centroid,
+                     scores, nb, sh.D, sh.G(), sh.per_group);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  SelArgs a;
+  a.scores = scores;
+  a.qn = q_norm;
+  a.kr = k_radius;
+  a.bound_out = bound_out;
+  a.gate_out = gate_out;
+  a.mask = mask;
+  a.counts = counts;
+  a.nb = nb;
+  a.nw = nw;
+  a.rows = rows;
+  a.G = sh.G();
+  a.per_group = sh.per_group;
+  a.top_k = cfg.top_k;
+  a.force_sink = cfg.force_sink;
+  a.gate = cfg.gate;
+  a.gate_factor = cfg.gate_factor;
+  a.gate_threshold = cfg.gate_threshold;
+  a.tau_log2e = cfg.temperature * kLog2e;
+  a.mass_threshold = cfg.mass_threshold;
+  a.rescue_fraction = cfg.rescue_fraction;
+  a.use_b = cfg.rescue_fraction > 0.0 ? 1 : 0;
+  a.use_p = cfg.mass_threshold > 0.0f ? 1 : 0;
+  a.per_wave_floats = nw * 64 * (1 + a.use_b + a.use_p);
+  const size_t per_wave_bytes = (size_t)a.per_wave_floats * sizeof(float);
+  int waves = (int)(65536 / per_wave_bytes);
+  waves = waves < 1 ? 1 : (waves > 4 ? 4 : waves);
+  hipLaunchKernelGGL(select_kernel, dim3((rows + waves - 1) / waves), dim3(64 * waves),
+                     waves * per_wave_bytes, stream, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, stream, counts, row_ptr, rows);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(compact_kernel, dim3((rows + 3) / 4), dim3(256), 0, stream, mask, row_ptr,
+                     col_idx, rows, nb, nw, col_capacity);
+  return hipGetLastError();
+}
+
+}  // namespace bsa

@@ -1,0 +1,202 @@
+/*
+ * bsa.h -- C ABI of the block-sparse attention prefill library (libbsa.so).
+ *
+ * Three calls make one prefill layer:
+ *
+ *   bsa_pool           mean-pooled query and key block centroids, query-centroid
+ *                      norms and key-block radii;
+ *   bsa_score_select   centroid block scores, then per selection row the kept key
+ *                      blocks (top-k with an optional uncertainty gate, a
+ *                      cumulative-mass base branch and a radius rescue branch,
+ *                      unioned with the forced blocks), emitted as CSR;
+ *   bsa_attention_fwd  online-softmax attention of every query block over its kept
+ *                      key blocks only, with the causal mask on the diagonal block.
+ *
+ * Sources (the method these calls compute):
+ *   - "Uncertainty-gated selection for block-sparse attention" (gist.science),
+ *     technical summary, Methodology steps 1-2 (block scores from mean-pooled
+ *     keys, per-tile top-k into a kv_idx list) and step 5 (expansion to top rho*k),
+ *     lay summary "The Solution" (a near tie of the best two doubles the budget).
+ *   - "RBS-Attention" (iaonda.com), third and fourth paragraphs: a base branch of
+ *     centroid relevance and a rescue branch using a dynamic key-block radius,
+ *     independent thresholds, masks fused, sparse FlashAttention downstream.
+ *   - "MiniMax presenta MSA" (iaonda.com), "What is MSA and how does it work": a
+ *     light index branch picks top-k KV blocks per GQA group; the main branch runs
+ *     attention over those blocks only.
+ *
+ * Conventions shared by every call
+ *   Layout: Q is [S, Hq, D], K and V are [S, Hkv, D], token-major and contiguous,
+ *   batch 1.  Blocks are B consecutive tokens; nb = ceil(S / B) and the last block
+ *   may be ragged (S - (nb-1)*B tokens).  Query head h reads kv head h / (Hq/Hkv).
+ *   A selection unit is a query head (BSA_SEL_PER_QHEAD, U = Hq) or a GQA group
+ *   (BSA_SEL_PER_GROUP, U = Hkv); a selection row is (unit u, query block i) and
+ *   rows are numbered u*nb + i.
+ *   FP8 inputs are OCP E4M3 codes (one byte each) with float32 scales [H, nb]:
+ *   value = decode(code) * scale[head][block].  BF16 inputs take no scales.
+ *   Supported now: head_dim in {64, 128}, block_size in {64, 128}.
+ *
+ *   Memory: every pointer argument is device memory allocated and owned by the
+ *   caller (16-byte aligned); the library never allocates or frees device memory
+ *   and never synchronises.  Host structs are read during the call only.
+ *
+ *   Streams: hip_stream is a hipStream_t passed as void* (NULL = null stream).
+ *   After host-side validation each call enqueues its kernels on that stream and
+ *   returns; results are ready when the stream reaches that point.
+ *
+ *   Errors: arguments are validated on the host before anything is launched; a
+ *   failing call launches nothing and returns a non-zero bsa_status, with a
+ *   message available from bsa_last_error() (thread-local).  BSA_ERR_DEVICE means
+ *   a launch failed (hipGetLastError); faults during execution surface at the
+ *   caller's next synchronisation.  seq_len == 0 is valid and launches nothing.
+ *   Calls are reentrant; concurrent calls on different streams do not interact.
+ */
+#ifndef BSA_H
+#define BSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BSA_ABI_VERSION 1
+
+typedef enum {
+  BSA_OK = 0,
+  BSA_ERR_INVALID_ARGUMENT = 1, /* null required pointer, bad shape or parameter */
+  BSA_ERR_UNSUPPORTED = 2,      /* valid but not implemented (e.g. head_dim 96)  */
+  BSA_ERR_CAPACITY = 3,         /* col_capacity below bsa_csr_capacity_bound      */
+  BSA_ERR_WORKSPACE = 4,        /* workspace smaller than required               */
+  BSA_ERR_DEVICE = 5            /* a kernel launch failed                        */
+} bsa_status;
+
+typedef enum { BSA_BF16 = 0, BSA_FP8_E4M3 = 1 } bsa_dtype;
+typedef enum { BSA_SEL_PER_QHEAD = 0, BSA_SEL_PER_GROUP = 1 } bsa_granularity;
+typedef enum { BSA_GATE_NONE = 0, BSA_GATE_TOP12_GAP = 1 } bsa_gate;
+
+/* Shape of one prefill layer. */
+typedef struct {
+  int64_t seq_len;      /* S >= 0                                              */
+  int32_t num_q_heads;  /* Hq >= 1                                             */
+  int32_t num_kv_heads; /* Hkv >= 1, Hq % Hkv == 0                             */
+  int32_t head_dim;     /* D                                                   */
+  int32_t block_size;   /* B                                                   */
+  int32_t dtype;        /* bsa_dtype of Q, K, V                                */
+  int32_t granularity;  /* bsa_granularity of the selection rows               */
+} bsa_problem;
+
+/* Selection rule.  Candidates of row (u, i) are C_i = {0..i} minus the forced
+ * blocks (the diagonal i, and block 0 when force_sink != 0); every branch ranks
+ * C_i by descending score with the lowest block index first on ties, and the
+ * kept set is the union of the forced blocks and every enabled branch. */
+typedef struct {
+  int32_t top_k;            /* k >= 0; 0 switches the top-k branch off          */
+  int32_t force_sink;       /* 0/1: also force block 0                          */
+  int32_t gate;             /* bsa_gate; applies to the top-k branch            */
+  float gate_threshold;     /* theta in (0, 1]: fires when p(0)-p(1) < theta   */
+  int32_t gate_factor;      /* rho >= 1: a fired row keeps rho*k                */
+  float score_temperature;  /* tau > 0 in softmax(tau * s) (gate and mass)     */
+  float mass_threshold;     /* mu in [0, 1]; 0 switches the base branch off    */
+  int32_t reserved;         /* must be 0                                        */
+  double rescue_fraction;   /* phi in [0, 1]; 0 switches the rescue branch off */
+} bsa_select_params;
+
+int bsa_abi_version(void);
+const char* bsa_status_string(int status);
+/* Detail of this thread's last failing call ("" if none). */
+const char* bsa_last_error(void);
+
+/* nb = ceil(S / B), or -1 if the problem is invalid. */
+int64_t bsa_num_blocks(const bsa_problem* problem);
+/* U * nb selection rows, or -1 if the problem is invalid. */
+int64_t bsa_num_select_rows(const bsa_problem* problem);
+
+/*
+ * bsa_pool -- block centroids ("Uncertainty-gated selection ...", Methodology
+ * step 1: keys grouped into blocks and scored by mean pooling; RBS-Attention,
+ * third paragraph: centroid relevance and a per-(prompt, layer, head) radius).
+ *
+ *   q, k         [S, Hq, D] / [S, Hkv, D] bf16, or E4M3 codes with q_scale [Hq, nb]
+ *                and k_scale [Hkv, nb] (required for FP8, ignored for BF16).
+ *   q_centroid   out [U, nb, D] f32: mean of the block's query rows; for per-group
+ *                rows the mean over the group's heads and the block's rows.
+ *   q_norm       out [U, nb] f32, ||q_centroid||_2 (nullable).
+ *   k_centroid   out [Hkv, nb, D] f32: mean of the block's key rows.
+ *   k_radius     out [Hkv, nb] f32: max over the block's keys of ||k - k_centroid||_2
+ *                (nullable; only the rescue branch needs it).
+ */
+bsa_status bsa_pool(const bsa_problem* problem, const void* q, const void* k,
+                    const float* q_scale, const float* k_scale, float* q_centroid,
+                    float* q_norm, float* k_centroid, float* k_radius, void* hip_stream);
+
+/* Upper bound on the total kept blocks over all rows (the col_idx length needed),
+ * computed from the parameters alone; -1 if the arguments are invalid. */
+int64_t bsa_csr_capacity_bound(const bsa_problem* problem, const bsa_select_params* params);
+
+/* Device workspace bytes bsa_score_select needs (0 on invalid arguments). */
+size_t bsa_score_select_workspace_size(const bsa_problem* problem,
+                                       const bsa_select_params* params, int export_scores);
+
+/*
+ * bsa_score_select -- block scores and kept-block lists.
+ *
+ * Score s[u][i][j] = q_centroid[u][i] . k_centroid[kv(u)][j] for j <= i
+ * ("Uncertainty-gated selection ...", Methodology step 1, the mean-pooling
+ * inner product).  Per row (u, i), with p = softmax(tau * s) over C_i:
+ *   top-k  : the first k of C_i; when gate == BSA_GATE_TOP12_GAP, |C_i| >= 2 and
+ *            p(0) - p(1) < theta, the first rho*k instead (same page, "The
+ *            Solution" and Methodology step 5);
+ *   base   : the shortest prefix of C_i whose mass reaches mu (RBS-Attention base
+ *            branch under its own threshold);
+ *   rescue : the first ceil(phi * |C_i|) of C_i ranked by the bound
+ *            b = s + q_norm[u][i] * k_radius[kv(u)][j] (RBS-Attention rescue branch);
+ *   kept   = forced U top-k U base U rescue, emitted ascending (diagonal last).
+ * Threshold decisions are taken in float32.
+ *
+ *   q_norm, k_radius  required when phi > 0, else nullable.
+ *   row_ptr      out int32 [U*nb + 1], exclusive prefix of the row lengths.
+ *   col_idx      out int32 [col_capacity]; col_capacity must be at least
+ *                bsa_csr_capacity_bound(), else BSA_ERR_CAPACITY.
+ *   scores_out   out f32 [U, nb, nb] (nullable): the scores the decisions used,
+ *                written for j <= i (other entries untouched).
+ *   bound_out    out f32 [U, nb, nb] (nullable): the rescue bounds, j <= i.
+ *   gate_out     out uint8 [U*nb] (nullable): 1 where the gate fired.
+ *   workspace    device scratch of at least
+ *                bsa_score_select_workspace_size(problem, params, scores_out != NULL)
+ *                bytes, else BSA_ERR_WORKSPACE.
+ */
+bsa_status bsa_score_select(const bsa_problem* problem, const bsa_select_params* params,
+                            const float* q_centroid, const float* q_norm,
+                            const float* k_centroid, const float* k_radius, int32_t* row_ptr,
+                            int32_t* col_idx, int64_t col_capacity, float* scores_out,
+                            float* bound_out, uint8_t* gate_out, void* workspace,
+                            size_t workspace_bytes, void* hip_stream);
+
+/*
+ * bsa_attention_fwd -- attention over the kept blocks (RBS-Attention, third
+ * paragraph: the fused mask drives sparse FlashAttention; MSA article: the main
+ * branch attends only over the preselected blocks).
+ *
+ * For query head h and token t in block i, with row (u(h), i) of the CSR:
+ *   O[t][h] = sum_s softmax_s(l_s) v_s over keys s <= t whose block is listed,
+ *   l_s = softmax_scale * q_t . k_s (FP8: times q_scale[h][i] * k_scale[g][j],
+ *   and v_s times v_scale[g][j]); lse[h][t] = log sum_s exp(l_s) (natural log).
+ *
+ *   row_ptr, col_idx  CSR as bsa_score_select writes it; each row's entries must
+ *                     be unique.  Entries outside [0, i] are ignored.  A token
+ *                     with no allowed key gets O = 0 and lse = -inf.
+ *   out               out bf16 [S, Hq, D].
+ *   lse               out f32 [Hq, S] (nullable).
+ */
+bsa_status bsa_attention_fwd(const bsa_problem* problem, const void* q, const void* k,
+                             const void* v, const float* q_scale, const float* k_scale,
+                             const float* v_scale, const int32_t* row_ptr,
+                             const int32_t* col_idx, float softmax_scale, void* out,
+                             float* lse, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSA_H */

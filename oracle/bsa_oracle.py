@@ -52,7 +52,7 @@ __all__ = [
     "pool_queries", "pool_keys", "block_scores", "rescue_bounds", "candidate_sets",
     "descending_order", "top_k", "gate_gap", "mass_prefix_length", "rescue_count",
     "select_row", "acceptable_row_sets", "select", "to_csr", "from_csr",
-    "attention_unit", "attention", "dense_causal_attention", "block_of", "unit_of_head",
+    "attend", "block_tokens", "attention_unit", "attention", "dense_causal_attention", "block_of", "unit_of_head",
     "kv_of_unit",
 ]
 
@@ -388,26 +388,32 @@ def from_csr(row_ptr, col_idx, U: int, nb: int):
 # paragraph, sparse FlashAttention over the fused mask; MSA article, the main
 # branch attends only over the preselected blocks)
 
-def attention_unit(Q, K, V, h: int, i: int, kept_blocks, B: int, scale: float, kvh: int):
-    """Output rows and log-sum-exp of query block i, head h, over the kept blocks.
-
-    For row t: allowed keys A_t = {s <= t : block(s) in kept}; logits l_s = scale *
-    q_t . k_s; O_t = sum_s softmax(l)_s v_s; lse_t = log sum_s exp(l_s) (natural log).
-    Written directly: all allowed logits at once, no running maximum.
-    """
-    S = Q.shape[0]
-    t0, t1 = i * B, min(S, (i + 1) * B)
-    keys = np.concatenate([np.arange(j * B, min(S, (j + 1) * B)) for j in kept_blocks])
-    q = Q[t0:t1, h, :]
-    logits = scale * (q @ K[keys, kvh, :].T)
-    allowed = keys[None, :] <= np.arange(t0, t1)[:, None]
+def attend(q: np.ndarray, q_pos: np.ndarray, k: np.ndarray, v: np.ndarray, k_pos: np.ndarray,
+           scale: float):
+    """Attention of query rows q (token positions q_pos) over key/value rows k, v
+    (positions k_pos): for row t, allowed keys A_t = {s : k_pos[s] <= q_pos[t]};
+    logits l_s = scale * q_t . k_s; O_t = sum_s softmax(l)_s v_s; lse_t = log sum_s
+    exp(l_s) (natural log).  Written directly: all allowed logits at once."""
+    logits = scale * (q @ k.T)
+    allowed = k_pos[None, :] <= q_pos[:, None]
     logits = np.where(allowed, logits, -np.inf)
     mx = logits.max(axis=1, keepdims=True)
     w = np.exp(logits - mx)
     z = w.sum(axis=1, keepdims=True)
-    out = (w / z) @ V[keys, kvh, :]
-    lse = (mx + np.log(z))[:, 0]
-    return out, lse
+    return (w / z) @ v, (mx + np.log(z))[:, 0]
+
+
+def block_tokens(blocks, B: int, S: int) -> np.ndarray:
+    """Token positions of the given blocks, in order (the last block may be ragged)."""
+    return np.concatenate([np.arange(j * B, min(S, (j + 1) * B)) for j in blocks])
+
+
+def attention_unit(Q, K, V, h: int, i: int, kept_blocks, B: int, scale: float, kvh: int):
+    """Output rows and log-sum-exp of query block i, head h, over the kept blocks."""
+    S = Q.shape[0]
+    t0, t1 = i * B, min(S, (i + 1) * B)
+    keys = block_tokens(kept_blocks, B, S)
+    return attend(Q[t0:t1, h, :], np.arange(t0, t1), K[keys, kvh, :], V[keys, kvh, :], keys, scale)
 
 
 def attention(Q, K, V, kept, B: int, scale: float, granularity: str, heads=None, blocks=None):

@@ -1,0 +1,169 @@
+"""C ABI checks that need no GPU: the library loads, exports every declared
+symbol, and rejects invalid arguments before any device call."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import block_sparse_attention_36_amd as bsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bsa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(bsa.LIB_PATH):
+        from block_sparse_attention_36_amd import build
+        build.build()
+    return bsa.load_library()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(bsa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    syms = declared_symbols()
+    assert len(syms) >= 9
+    for s in syms:
+        assert hasattr(lib, s), s
+
+
+def test_version_and_status_strings(lib):
+    assert lib.bsa_abi_version() == 1
+    assert lib.bsa_status_string(0) == b"ok"
+    assert lib.bsa_status_string(3) == b"CSR capacity too small"
+
+
+def _prob(**kw):
+    d = dict(seq_len=4096, num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=128,
+             dtype=bsa.BSA_BF16, granularity=bsa.BSA_SEL_PER_QHEAD)
+    d.update(kw)
+    return bsa.Problem(**d)
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(seq_len=-1), 1), (dict(num_q_heads=0), 1), (dict(num_q_heads=6, num_kv_heads=4), 1),
+    (dict(head_dim=96), 2), (dict(block_size=32), 2), (dict(dtype=7), 1),
+    (dict(granularity=3), 1),
+])
+def test_pool_rejects_bad_problems(lib, kw, status):
+    p = _prob(**kw)
+    st = lib.bsa_pool(ctypes.byref(p), FAKE, FAKE, None, None, FAKE, None, FAKE, None, None)
+    assert st == status
+    assert lib.bsa_last_error() != b""
+
+
+def test_pool_requires_pointers_and_fp8_scales(lib):
+    p = _prob()
+    assert lib.bsa_pool(ctypes.byref(p), None, FAKE, None, None, FAKE, None, FAKE, None, None) == 1
+    p8 = _prob(dtype=bsa.BSA_FP8_E4M3)
+    assert lib.bsa_pool(ctypes.byref(p8), FAKE, FAKE, None, None, FAKE, None, FAKE, None,
+                        None) == 1
+    assert b"scale" in lib.bsa_last_error()
+
+
+@pytest.mark.parametrize("kw", [dict(top_k=-1), dict(gate=5), dict(gate=1, gate_threshold=0.0),
+                                dict(gate=1, gate_factor=0), dict(score_temperature=0.0),
+                                dict(mass_threshold=1.5), dict(rescue_fraction=-0.1),
+                                dict(force_sink=2)])
+def test_select_rejects_bad_params(lib, kw):
+    p = _prob()
+    d = dict(top_k=4, force_sink=1)
+    d.update(kw)
+    s = bsa.make_params(**d)
+    s.force_sink = d["force_sink"]  # make_params would normalise it to 0/1
+    st = lib.bsa_score_select(ctypes.byref(p), ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE,
+                              FAKE, 10**9, None, None, None, FAKE, 10**12, None)
+    assert st == 1
+    assert lib.bsa_csr_capacity_bound(ctypes.byref(p), ctypes.byref(s)) == -1
+
+
+def test_select_capacity_and_workspace_errors(lib):
+    p = _prob()
+    s = bsa.make_params(top_k=4, force_sink=1)
+    cap = lib.bsa_csr_capacity_bound(ctypes.byref(p), ctypes.byref(s))
+    ws = lib.bsa_score_select_workspace_size(ctypes.byref(p), ctypes.byref(s), 0)
+    assert cap > 0 and ws > 0
+    st = lib.bsa_score_select(ctypes.byref(p), ctypes.byref(s), FAKE, None, FAKE, None, FAKE,
+                              FAKE, cap - 1, None, None, None, FAKE, ws, None)
+    assert st == 3
+    st = lib.bsa_score_select(ctypes.byref(p), ctypes.byref(s), FAKE, None, FAKE, None, FAKE,
+                              FAKE, cap, None, None, None, FAKE, ws - 1, None)
+    assert st == 4
+    # the rescue branch needs norms and radii
+    s2 = bsa.make_params(rescue_fraction=0.05)
+    cap2 = lib.bsa_csr_capacity_bound(ctypes.byref(p), ctypes.byref(s2))
+    st = lib.bsa_score_select(ctypes.byref(p), ctypes.byref(s2), FAKE, None, FAKE, None, FAKE,
+                              FAKE, cap2, None, None, None, FAKE, 10**12, None)
+    assert st == 1
+
+
+def test_capacity_bound_covers_any_selection(lib):
+    """The bound is the sum over rows of the largest kept set the parameters allow;
+    check it against the oracle's kept sets on random scores."""
+    from oracle import bsa_oracle as O
+    rng = np.random.default_rng(0)
+    for gate, mass, resc, sink in [(0, 0.0, 0.0, 1), (1, 0.0, 0.0, 1), (0, 0.9, 0.05, 0),
+                                   (0, 0.0, 0.2, 0)]:
+        nb = 21
+        p = _prob(seq_len=nb * 128 - 5, num_q_heads=2, num_kv_heads=1)
+        s = bsa.make_params(top_k=3, force_sink=sink, gate=gate, gate_threshold=0.5,
+                            mass_threshold=mass, rescue_fraction=resc)
+        bound = lib.bsa_csr_capacity_bound(ctypes.byref(p), ctypes.byref(s))
+        op = O.SelectParams(top_k=3, force_sink=bool(sink), gate="top12_gap" if gate else "none",
+                            gate_threshold=0.5, mass_threshold=mass,
+                            rescue_fraction=resc).as_library_precision()
+        total = 0
+        for u in range(2):
+            for i in range(nb):
+                sc = rng.normal(0, 0.3, size=i + 1)
+                kept, _ = O.select_row(i, sc, sc + rng.uniform(0, 2, size=i + 1), op)
+                total += len(kept)
+        assert total <= bound
+
+
+def test_attention_rejects_bad_arguments(lib):
+    p = _prob()
+    st = lib.bsa_attention_fwd(ctypes.byref(p), FAKE, FAKE, None, None, None, None, FAKE, FAKE,
+                               0.1, FAKE, None, None)
+    assert st == 1
+    st = lib.bsa_attention_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, None, None, None, FAKE, FAKE,
+                               float("nan"), FAKE, None, None)
+    assert st == 1
+    p8 = _prob(dtype=bsa.BSA_FP8_E4M3)
+    st = lib.bsa_attention_fwd(ctypes.byref(p8), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE,
+                               0.1, FAKE, None, None)
+    assert st == 1
+
+
+def test_empty_sequence_launches_nothing(lib):
+    p = _prob(seq_len=0)
+    assert lib.bsa_num_blocks(ctypes.byref(p)) == 0
+    assert lib.bsa_pool(ctypes.byref(p), None, None, None, None, None, None, None, None,
+                        None) == 0
+
+
+def test_counts(lib):
+    p = _prob(seq_len=1000, block_size=64, head_dim=64, num_q_heads=4, num_kv_heads=2,
+              granularity=bsa.BSA_SEL_PER_GROUP)
+    assert lib.bsa_num_blocks(ctypes.byref(p)) == 16
+    assert lib.bsa_num_select_rows(ctypes.byref(p)) == 32
+
+
+def test_binding_raises_without_library(tmp_path):
+    saved = bsa._lib
+    bsa._lib = None
+    try:
+        with pytest.raises(RuntimeError):
+            bsa.load_library(str(tmp_path / "missing.so"))
+    finally:
+        bsa._lib = saved
