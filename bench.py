@@ -147,6 +147,47 @@ def cpu_baseline(cfg, inp, sel_rows, budget_s: float = 15.0):
             "seconds": round(el, 2)}
 
 
+COPY_BYTES = 1 << 30
+
+
+def _pmc_rows(d: str, counter: str):
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r.get("Counter_Name") == counter:
+                rows.append(r)
+    return rows
+
+
+def summarize_pmc(fetch_dir: str, write_dir: str, out_json: str) -> int:
+    """HBM bytes per attention launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
+    each scaled by what the same counter reads for a plain copy of COPY_BYTES."""
+    import statistics
+    out = {"kernel": "attn_fwd_kernel<128, 128, false>", "workload": "dual128k",
+           "kernel_source_hash": source_hash("attention.hip", "common.h")}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _pmc_rows(d, counter)
+        att = [float(r["Counter_Value"]) * 1024 for r in rows if "attn_fwd_kernel" in r["Kernel_Name"]]
+        cp = [float(r["Counter_Value"]) * 1024 for r in rows
+              if "copy" in r["Kernel_Name"].lower() and float(r["Counter_Value"]) * 1024 > COPY_BYTES / 2]
+        if not att or not cp:
+            print(f"missing {counter} rows (attention {len(att)}, copy {len(cp)})", file=sys.stderr)
+            return 1
+        factor = statistics.mean(cp) / COPY_BYTES
+        out[counter.lower()] = {"raw_bytes_per_launch": statistics.mean(att),
+                                "copy_raw_bytes": statistics.mean(cp), "copy_bytes": COPY_BYTES,
+                                "scale": factor,
+                                "bytes_per_launch": statistics.mean(att) / factor}
+    out["hbm_bytes_per_launch"] = (out["fetch_size"]["bytes_per_launch"] +
+                                   out["write_size"]["bytes_per_launch"])
+    with open(out_json, "w") as f:
+        json.dump(out, f, indent=2)
+    print(json.dumps(out))
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -155,7 +196,14 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default="dual128k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after timing, run one plain device copy of 1 GiB (counter calibration)")
+    ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT_JSON"),
+                    help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) into HBM bytes "
+                         "per attention launch, calibrated on the 1 GiB copy; no GPU needed")
     args = ap.parse_args(argv)
+    if args.summarize_pmc:
+        return summarize_pmc(*args.summarize_pmc)
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (asked for {args.gpus}): the block-sparse "
               "prefill path here has no multi-GPU mode.", file=sys.stderr)
@@ -210,10 +258,6 @@ def main(argv=None) -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    rp = bufs.row_ptr.cpu().numpy()
-    nnz = int(rp[-1])
-    ci = bufs.col_idx[:nnz].cpu().numpy()
-    kept_flops = attention_flops(rp, ci, cfg)
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
@@ -223,6 +267,10 @@ def main(argv=None) -> int:
         step(evs[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    rp = bufs.row_ptr.cpu().numpy()  # the CSR of the timed steps (deterministic)
+    nnz = int(rp[-1])
+    ci = bufs.col_idx[:nnz].cpu().numpy()
+    kept_flops = attention_flops(rp, ci, cfg)
     pool_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     sel_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
     att_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
@@ -269,6 +317,13 @@ def main(argv=None) -> int:
                         "gbs": round(ps_bytes / (ps_ms * 1e-3) / 1e9, 1),
                         "frac_hbm": round(ps_bytes / (ps_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
     }
+    if args.calibrate_copy:
+        src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(cfg, inp, None, args.cpu_seconds)

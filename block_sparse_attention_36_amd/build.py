@@ -4,7 +4,9 @@
 
 Every HIP source is compiled to an object in parallel, then linked into
 ``block_sparse_attention_36_amd/libbsa.so`` next to this file.  Packed fp32
-VALU instructions are disabled for device code (``-packed-fp32-ops``).
+VALU instructions are disabled for device code (``-packed-fp32-ops``), and MFMA
+accumulators may live in VGPRs (``-amdgpu-mfma-vgpr-form``), which the
+attention kernel relies on to feed scores to the VALU without copies.
 """
 
 from __future__ import annotations
@@ -27,6 +29,7 @@ ARCH = os.environ.get("BSA_OFFLOAD_ARCH", "gfx950")
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
     "-Wno-unused-command-line-argument",
 ]

@@ -134,22 +134,14 @@ struct Stage {
   static constexpr int LDS_BYTES = FP8 ? 2 * RAW_STAGE + C::STAGE : 2 * C::STAGE;
   static_assert(NI >= 1 && RAW_TILE % 4096 == 0, "tile must split into 1 KiB DMAs per wave");
 
-  // DMA key block j of kv head g into raw stage `dst` (K tile then V tile).  K and
-  // V share the per-lane offsets; rows past the ragged end re-read the last row
-  // (their logits are masked).
-  static __device__ __forceinline__ void issue(const AttnArgs& a, int g, int j, unsigned char* dst,
-                                               int wave, int l) {
-    constexpr int ES = FP8 ? 1 : 2;                      // bytes per element
-    const unsigned rs = (unsigned)(a.Hkv * D * ES);      // bytes per token row
-    const size_t blk = ((size_t)j * B * a.Hkv + (size_t)g) * D * ES;
-    const unsigned char* kb = (const unsigned char*)a.k + blk;
-    const unsigned char* vb = (const unsigned char*)a.v + blk;
-    const int64_t left = a.S - (int64_t)j * B;
-    const int rmax = left < B ? (int)left - 1 : B - 1;
+  // Per-lane byte offsets of the NI DMA instructions inside one tile (row r of the
+  // tile at r * rs, chunk swizzled for bf16), shared by K and V; computed once.
+  static __device__ __forceinline__ void plan(const AttnArgs& a, int wave, int l, unsigned* off) {
+    constexpr int ES = FP8 ? 1 : 2;
+    const unsigned rs = (unsigned)(a.Hkv * D * ES);
 #pragma unroll
     for (int n = 0; n < NI; ++n) {
-      const int base = (wave * NI + n) * 1024;
-      const int p = base + 16 * l;
+      const int p = (wave * NI + n) * 1024 + 16 * l;
       int r, col;  // tile row and byte column of this lane's 16 bytes
       if (!FP8) {
         r = p / C::ROWB;
@@ -158,9 +150,37 @@ struct Stage {
         r = p / D;
         col = p % D;
       }
-      const unsigned off = (unsigned)(r < rmax ? r : rmax) * rs + (unsigned)col;
-      dma16(kb, off, lds_addr(dst + base));
-      dma16(vb, off, lds_addr(dst + RAW_TILE + base));
+      off[n] = (unsigned)r * rs + (unsigned)col;
+    }
+  }
+
+  // DMA key block j of kv head g into raw stage `dst` (K tile then V tile).  Rows
+  // past the ragged end re-read the last row (their logits are masked).
+  static __device__ __forceinline__ void issue(const AttnArgs& a, int g, int j, unsigned char* dst,
+                                               int wave, int l, const unsigned* off) {
+    constexpr int ES = FP8 ? 1 : 2;
+    const size_t blk = ((size_t)j * B * a.Hkv + (size_t)g) * D * ES;
+    const unsigned char* kb = (const unsigned char*)a.k + blk;
+    const unsigned char* vb = (const unsigned char*)a.v + blk;
+    const int64_t left = a.S - (int64_t)j * B;
+    if (left >= B) {
+#pragma unroll
+      for (int n = 0; n < NI; ++n) {
+        const int base = (wave * NI + n) * 1024;
+        dma16(kb, off[n], lds_addr(dst + base));
+        dma16(vb, off[n], lds_addr(dst + RAW_TILE + base));
+      }
+    } else {
+      const unsigned rs = (unsigned)(a.Hkv * D * ES);
+      const unsigned last = (unsigned)(left - 1) * rs;  // ragged block: clamp the row
+#pragma unroll
+      for (int n = 0; n < NI; ++n) {
+        const int base = (wave * NI + n) * 1024;
+        const unsigned col = off[n] % rs, rowoff = off[n] - col;
+        const unsigned o = (rowoff < last ? rowoff : last) + col;
+        dma16(kb, o, lds_addr(dst + base));
+        dma16(vb, o, lds_addr(dst + RAW_TILE + base));
+      }
     }
   }
 
@@ -187,6 +207,53 @@ struct Stage {
   }
 };
 
+// exp2 of key tile kt2 for every query tile: p = 2^(s*sl - m), summed per query,
+// scaled by vsc (E4M3 value scale) and packed to the bf16 B operands of two steps.
+template <int D, int B>
+__device__ __forceinline__ void probs(f32x16 (&s)[B / 64][B / 64], int kt2, const float* nref,
+                                      float sl, float vsc, float* psum, u32x4 (&pk)[2][B / 64]) {
+  typedef Cfg<D, B> C;
+#pragma unroll
+  for (int qt = 0; qt < C::NQT; ++qt) {
+    float p[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      p[v] = __builtin_amdgcn_exp2f(fmaf(s[kt2][qt][v], sl, nref[qt]));
+      psum[qt] += p[v];
+    }
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        pk[sb][qt][e] = pack_bf16x2(p[8 * sb + 2 * e] * vsc, p[8 * sb + 2 * e + 1] * vsc);
+  }
+}
+
+// O^T += V^T P^T over the two 16-key steps of key tile kt2.  The key rows of one
+// step are 4*hf + [0,4) (elements 0..3) and the same + 8 (elements 4..7); their
+// swizzle does not depend on the step, so the step offset folds into the read.
+template <int D, int B>
+__device__ __forceinline__ void pv_tile(const unsigned char* vrow, const u32x4 (&pk)[2][B / 64],
+                                        f32x16 (&o)[D / 32][B / 64], int kt2, int rlo, int cb0) {
+  typedef Cfg<D, B> C;
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb) {
+    const int step = (kt2 * 32 + sb * 16) * C::ROWB;
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt) {
+      const int c = (dt * 64 + cb0) >> 4;  // chunk of this lane's 8 bytes
+      const s16x4 lo = lds_read_tr16(vrow + step + ((c ^ swz<D>(rlo)) << 4));
+      const s16x4 hi = lds_read_tr16(vrow + 8 * C::ROWB + step + ((c ^ swz<D>(rlo + 8)) << 4));
+      const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+      const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{lo2[0], lo2[1], hi2[0], hi2[1]});
+#pragma unroll
+      for (int qt = 0; qt < C::NQT; ++qt)
+        o[dt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            vf, __builtin_bit_cast(bf16x8, pk[sb][qt]), o[dt][qt], 0, 0, 0);
+    }
+  }
+}
+
 template <int D, int B, bool FP8>
 __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
   typedef Cfg<D, B> C;
@@ -196,15 +263,18 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qh = wave & 1, kh = wave >> 1, hf = l >> 5;
 
-  // ---- (head, query block) of this workgroup: heads of one group at one query
-  // block share an XCD (workgroup id mod 8); rows go longest first.
+  // ---- (head, query block) of this workgroup.  Rows are ordered kv-head major
+  // (the whole chip works through one kv head's K/V at a time, a working set
+  // that stays resident in the last-level cache), longest query block first
+  // within a kv head, and the heads of one group at one query block share an
+  // XCD (workgroup id mod 8) so their common K/V blocks meet in one L2.
   const int G = a.Hq / a.Hkv, nb = a.nb;
   const int bid = blockIdx.x;
   const int xcd = bid & 7, t8 = bid >> 3;
   const int hh = t8 % G;
   const int r = (t8 / G) * 8 + xcd;
   if (r >= a.Hkv * nb) return;  // padding workgroup (uniform: no barrier reached)
-  const int i = nb - 1 - r / a.Hkv, g = r % a.Hkv;
+  const int g = r / nb, i = nb - 1 - r % nb;
   const int h = g * G + hh;
   const int unit = a.per_group ? g : h;
   const int row = unit * nb + i;
@@ -214,9 +284,11 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
     const int j = a.col_idx[e0 + n];
     return (j >= 0 && j <= i) ? j : -1;  // -1: entry outside the causal range, skipped
   };
+  unsigned doff[ST::NI];
+  ST::plan(a, wave, l, doff);
   if (nblk > 0) {
     const int j0 = block_at(0);
-    ST::issue(a, g, j0 < 0 ? 0 : j0, lds, wave, l);
+    ST::issue(a, g, j0 < 0 ? 0 : j0, lds, wave, l, doff);
   }
 
   // ---- Q fragments (B operand of S^T = K Q^T): query column = lane % 32,
@@ -256,7 +328,7 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
     unsigned char* raw = lds + (n & 1) * ST::RAW_STAGE;
     if (n + 1 < nblk) {
       const int jn = block_at(n + 1);
-      ST::issue(a, g, jn < 0 ? 0 : jn, lds + ((n + 1) & 1) * ST::RAW_STAGE, wave, l);
+      ST::issue(a, g, jn < 0 ? 0 : jn, lds + ((n + 1) & 1) * ST::RAW_STAGE, wave, l, doff);
       wait_vmcnt<ST::NPW>();  // this wave's DMAs of block n have landed
     } else {
       wait_vmcnt<0>();
@@ -308,8 +380,10 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
       const bool masked = (j == i) || ((int64_t)j * B + kh * C::KW + C::KW > a.S);
       const int kfirst = kh * C::KW + hf * 4;
       const int64_t left = a.S - (int64_t)j * B - 1 - kfirst;  // last valid kw
+      float nref[C::NQT];
 #pragma unroll
       for (int qt = 0; qt < C::NQT; ++qt) {
+        // block max on the raw scores (sl > 0), then one FMA + exp2 per element
         float mx = -INFINITY;
         if (masked) {
           const int qi = qh * C::QW + qt * 32 + (l & 31);  // query index in the block
@@ -320,7 +394,7 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
               const int kw = kt2 * 32 + (v >> 2) * 8 + (v & 3);
-              const float x = kw > lim ? -INFINITY : s[kt2][qt][v] * sl;
+              const float x = kw > lim ? -INFINITY : s[kt2][qt][v];
               s[kt2][qt][v] = x;
               mx = fmaxf(mx, x);
             }
@@ -328,73 +402,40 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
           for (int kt2 = 0; kt2 < C::NKT; ++kt2)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              const float x = s[kt2][qt][v] * sl;
-              s[kt2][qt][v] = x;
-              mx = fmaxf(mx, x);
-            }
+            for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kt2][qt][v]);
         }
-        mx = max_with_other_half(mx);
+        mx = max_with_other_half(mx) * sl;
         const bool bump = mx > m[qt] + 8.0f;  // also true for the first finite block max
         if (__ballot(bump)) {
-          const float mnew = bump ? mx : m[qt];
-          const float alpha = exp2f(m[qt] - mnew);  // 0 when m was -inf
-          m[qt] = mnew;
+          // lanes that do not move keep alpha = 1 (their max may still be -inf)
+          const float alpha = bump ? __builtin_amdgcn_exp2f(m[qt] - mx) : 1.0f;  // 0 from -inf
+          m[qt] = bump ? mx : m[qt];
           lsum[qt] *= alpha;
 #pragma unroll
           for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
             for (int v = 0; v < 16; ++v) o[dt][qt][v] *= alpha;
         }
-        const float mref = m[qt] == -INFINITY ? 0.f : m[qt];
-        float ps = 0.f;
-#pragma unroll
-        for (int kt2 = 0; kt2 < C::NKT; ++kt2)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const float p = exp2f(s[kt2][qt][v] - mref);
-            ps += p;
-            s[kt2][qt][v] = p;
-          }
-        lsum[qt] += ps;
+        nref[qt] = m[qt] == -INFINITY ? 0.f : -m[qt];
       }
 
-      // ---- O^T += V^T P^T: A = V^T (d rows, transposing LDS read), B = P^T.
-      // Key rows of one step are k0 + 4*hf + [0,4) (elements 0..3) and the same
-      // +8 (elements 4..7); their swizzle does not depend on the step, so the
-      // step offset folds into the instruction and only the d tile and the
-      // lo/hi half select a lane address.
+      // ---- exp2 + bf16 packing of key tile 0, then O^T += V^T P^T for tile 0 while
+      // the VALU turns key tile 1 into probabilities (independent work, same block)
+      float psum[C::NQT];
+#pragma unroll
+      for (int qt = 0; qt < C::NQT; ++qt) psum[qt] = 0.f;
       const int rlo = 4 * hf + ((l & 15) >> 2);  // row within a 16-key step
       const int cb0 = (((l >> 4) & 1) * 16 + 4 * (l & 3)) * 2;  // byte column in a d tile
       const unsigned char* vrow = vt + (kh * C::KW + rlo) * C::ROWB + (cb0 & 15);
-#pragma unroll
-      for (int ks = 0; ks < C::NKS; ++ks) {
-        const int kt2 = ks >> 1, sb = ks & 1;
-        bf16x8 pf[C::NQT];
-#pragma unroll
-        for (int qt = 0; qt < C::NQT; ++qt) {
-          u32x4 pk;
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            pk[e] = pack_bf16x2(s[kt2][qt][8 * sb + 2 * e] * vsc,
-                                s[kt2][qt][8 * sb + 2 * e + 1] * vsc);
-          pf[qt] = __builtin_bit_cast(bf16x8, pk);
-        }
-        const int step = (kt2 * 32 + sb * 16) * C::ROWB;
-#pragma unroll
-        for (int dt = 0; dt < C::NDT; ++dt) {
-          const int c = (dt * 64 + cb0) >> 4;  // chunk of this lane's 8 bytes
-          const s16x4 lo =
-              lds_read_tr16(vrow + step + ((c ^ swz<D>(rlo)) << 4));
-          const s16x4 hi =
-              lds_read_tr16(vrow + 8 * C::ROWB + step + ((c ^ swz<D>(rlo + 8)) << 4));
-          const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
-          const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{lo2[0], lo2[1], hi2[0], hi2[1]});
-#pragma unroll
-          for (int qt = 0; qt < C::NQT; ++qt)
-            o[dt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qt], o[dt][qt], 0, 0, 0);
-        }
+      u32x4 pk0[2][C::NQT], pk1[2][C::NQT];
+      probs<D, B>(s, 0, nref, sl, vsc, psum, pk0);
+      pv_tile<D, B>(vrow, pk0, o, 0, rlo, cb0);
+      if (C::NKT > 1) {
+        probs<D, B>(s, C::NKT - 1, nref, sl, vsc, psum, pk1);
+        pv_tile<D, B>(vrow, pk1, o, C::NKT - 1, rlo, cb0);
       }
+#pragma unroll
+      for (int qt = 0; qt < C::NQT; ++qt) lsum[qt] += psum[qt];
     }
     lds_barrier();  // every wave is done with this stage before it is refilled
   }

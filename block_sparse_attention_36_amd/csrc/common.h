@@ -32,15 +32,11 @@ __device__ __forceinline__ float max_with_other_half(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// Round-to-nearest-even float -> bf16 bits (inputs here are finite).
-__device__ __forceinline__ unsigned short f32_to_bf16_bits(float f) {
-  unsigned u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (unsigned short)(u >> 16);
-}
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 
+// Two floats -> two bf16 (round to nearest even) in one dword: V_CVT_PK_BF16_F32.
 __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
-  return (unsigned)f32_to_bf16_bits(lo) | ((unsigned)f32_to_bf16_bits(hi) << 16);
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{lo, hi}, bf16x2_t));
 }
 
 __device__ __forceinline__ float bf16_bits_to_f32(unsigned short b) {
@@ -49,7 +45,6 @@ __device__ __forceinline__ float bf16_bits_to_f32(unsigned short b) {
 
 // OCP E4M3 decoding with the gfx950 conversion instructions (exact for every
 // code: E4M3 values are representable in both bf16 and fp32).
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 
 // Four E4M3 codes (one dword) -> four bf16 packed in two dwords.
 __device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(unsigned w) {
