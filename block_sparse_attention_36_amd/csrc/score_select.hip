@@ -289,10 +289,257 @@ __global__ __launch_bounds__(256) void select_kernel(SelArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ selection, register form
+// Rows of up to 64*SPL blocks keep their order-preserving keys in registers
+// (slot e of lane l holds block j = 64e + l).  A threshold probe is then one
+// compare per slot plus a ballot popcount (scalar), with no LDS traffic and no
+// cross-lane reduction; the base branch extracts maxima one at a time in the
+// ranking order (the usual case needs a handful) and falls back to bisection
+// on fixed-tree mass sums when more than 16 blocks are needed.
+
+__device__ __forceinline__ float key_float(unsigned k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+template <int SPL>
+struct RowKeys {
+  static_assert(SPL >= 1 && SPL <= 64, "one bit per slot in a 64-bit mask");
+  unsigned k[SPL];
+  unsigned long long cand_bits;  // bit e: slot e of this lane is a candidate
+  __device__ __forceinline__ bool cand(int e) const { return (cand_bits >> e) & 1ull; }
+};
+
+// number of candidates with key >= x (wave-uniform)
+template <int SPL>
+__device__ __forceinline__ int count_ge_reg(const RowKeys<SPL>& r, int nsl, unsigned x) {
+  int c = 0;
+#pragma unroll
+  for (int e = 0; e < SPL; ++e)
+    if (e < nsl) c += __popcll(ballot64(r.cand(e) && r.k[e] >= x));
+  return c;
+}
+
+template <int SPL>
+__device__ void topk_reg(const RowKeys<SPL>& r, int nsl, int nc, int k, unsigned& T, int& need) {
+  if (k >= nc) {
+    T = 0u;
+    need = nc;
+    return;
+  }
+  if (k <= 0) {
+    T = 0xFFFFFFFFu;
+    need = 0;
+    return;
+  }
+  unsigned t = 0u;
+  for (int bit = 31; bit >= 0; --bit) {
+    const unsigned x = t | (1u << bit);
+    if (count_ge_reg(r, nsl, x) >= k) t = x;
+  }
+  need = k - (t == 0xFFFFFFFFu ? 0 : count_ge_reg(r, nsl, t + 1u));
+  T = t;
+}
+
+template <int SPL>
+__global__ __launch_bounds__(256) void select_reg_kernel(SelArgs a) {
+  const int l = lane_id();
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= a.rows) return;  // no workgroup barriers below
+  const int nb = a.nb;
+  const int u = row / nb, i = row % nb;
+  const int g = a.per_group ? u : u / a.G;
+  const int sink = a.force_sink;
+  const int nc = i > 0 ? i - (sink ? 1 : 0) : 0;
+  const int nsl = i / 64 + 1;
+  const float* srow = a.scores + ((size_t)u * nb + i) * nb;
+  const float qnv = a.use_b ? a.qn[(size_t)u * nb + i] : 0.f;
+
+  RowKeys<SPL> sr, br;
+  sr.cand_bits = 0ull;
+#pragma unroll
+  for (int e = 0; e < SPL; ++e) {
+    sr.k[e] = 0u;
+    br.k[e] = 0u;
+    const int j = e * 64 + l;
+    if (e < nsl && j <= i) {
+      const float sv = srow[j];
+      sr.k[e] = float_key(sv);
+      if (a.use_b) {
+        const float bv = fmaf(qnv, a.kr[(size_t)g * nb + j], sv);
+        br.k[e] = float_key(bv);
+        if (a.bound_out) a.bound_out[((size_t)u * nb + i) * nb + j] = bv;
+      }
+      if (is_cand(j, i, sink)) sr.cand_bits |= 1ull << e;
+    }
+  }
+  br.cand_bits = sr.cand_bits;
+
+  // softmax statistics over the candidates (gate and mass)
+  float s0 = -INFINITY, zsum = 0.f;
+  unsigned kmax = 0u;
+  const bool need_soft = (a.gate && a.top_k > 0) || a.use_p;
+  if (need_soft && nc > 0) {
+    unsigned km = 0u;
+#pragma unroll
+    for (int e = 0; e < SPL; ++e)
+      if (e < nsl && sr.cand(e)) km = max(km, sr.k[e]);
+    for (int o = 32; o >= 1; o >>= 1) km = max(km, (unsigned)__shfl_xor((int)km, o));
+    kmax = km;
+    s0 = key_float(kmax);
+    float z = 0.f;
+#pragma unroll
+    for (int e = 0; e < SPL; ++e)
+      if (e < nsl && sr.cand(e)) z += exp2f((key_float(sr.k[e]) - s0) * a.tau_log2e);
+    zsum = wave_sum(z);
+  }
+
+  // top-k branch (with the optional gate)
+  unsigned Tk = 0xFFFFFFFFu;
+  int needk = 0;
+  bool fired = false;
+  if (a.top_k > 0) {
+    if (a.gate && nc >= 2) {
+      int jm = 0x7FFFFFFF;
+#pragma unroll
+      for (int e = SPL - 1; e >= 0; --e)
+        if (e < nsl && sr.cand(e) && sr.k[e] == kmax) jm = e * 64 + l;
+      for (int o = 32; o >= 1; o >>= 1) jm = min(jm, __shfl_xor(jm, o));
+      unsigned k2 = 0u;
+#pragma unroll
+      for (int e = 0; e < SPL; ++e)
+        if (e < nsl && sr.cand(e) && e * 64 + l != jm) k2 = max(k2, sr.k[e]);
+      for (int o = 32; o >= 1; o >>= 1) k2 = max(k2, (unsigned)__shfl_xor((int)k2, o));
+      const float gap = (1.0f - exp2f((key_float(k2) - s0) * a.tau_log2e)) / zsum;
+      fired = gap < a.gate_threshold;
+    }
+    topk_reg(sr, nsl, nc, a.top_k * (fired ? a.gate_factor : 1), Tk, needk);
+  }
+
+  // base branch: shortest prefix of the ranking whose mass reaches mu
+  unsigned long long taken = 0ull;  // extraction result (bits per slot of this lane)
+  bool by_extraction = true;
+  unsigned Tm = 0xFFFFFFFFu;
+  int needm = 0;
+  if (a.use_p && nc > 0) {
+    float cum = 0.f;
+    int steps = 0;
+    bool done = false;
+    while (!done && steps < 16) {
+      unsigned bk = 0u;
+      int bj = 0x7FFFFFFF;
+#pragma unroll
+      for (int e = 0; e < SPL; ++e)
+        if (e < nsl && sr.cand(e) && !((taken >> e) & 1ull) && sr.k[e] > bk) {
+          bk = sr.k[e];
+          bj = e * 64 + l;
+        }
+      for (int o = 32; o >= 1; o >>= 1) {
+        const unsigned ok = (unsigned)__shfl_xor((int)bk, o);
+        const int oj = __shfl_xor(bj, o);
+        if (ok > bk || (ok == bk && oj < bj)) {
+          bk = ok;
+          bj = oj;
+        }
+      }
+      if (bj == 0x7FFFFFFF) break;  // every candidate taken
+      cum += exp2f((key_float(bk) - s0) * a.tau_log2e) / zsum;
+      if ((bj & 63) == l) taken |= 1ull << (bj >> 6);
+      ++steps;
+      done = cum >= a.mass_threshold;
+    }
+    if (!done && __popcll(ballot64(taken != 0ull)) >= 0 && steps >= 16) {
+      // many blocks needed: bisection on the mass of {key >= x} (fixed-tree sums)
+      by_extraction = false;
+      auto mass_ge = [&](unsigned x) {
+        float m = 0.f;
+#pragma unroll
+        for (int e = 0; e < SPL; ++e)
+          if (e < nsl && sr.cand(e) && sr.k[e] >= x)
+            m += exp2f((key_float(sr.k[e]) - s0) * a.tau_log2e) / zsum;
+        return wave_sum(m);
+      };
+      unsigned t = 0u;
+      for (int bit = 31; bit >= 0; --bit) {
+        const unsigned x = t | (1u << bit);
+        if (mass_ge(x) >= a.mass_threshold) t = x;
+      }
+      if (mass_ge(t) < a.mass_threshold) {
+        Tm = 0u;
+        needm = nc;
+      } else {
+        Tm = t;
+        float c2 = (t == 0xFFFFFFFFu) ? 0.f : mass_ge(t + 1u);
+#pragma unroll
+        for (int e = 0; e < SPL; ++e) {
+          if (e >= nsl || c2 >= a.mass_threshold) continue;
+          unsigned long long tie = ballot64(sr.cand(e) && sr.k[e] == t);
+          while (tie && c2 < a.mass_threshold) {
+            const int src = __builtin_ctzll(tie);
+            c2 += exp2f((key_float(t) - s0) * a.tau_log2e) / zsum;
+            ++needm;
+            tie &= tie - 1;
+            (void)src;
+          }
+        }
+      }
+    }
+  }
+
+  // rescue branch: top ceil(phi*|C_i|) by the bound
+  unsigned Tr = 0xFFFFFFFFu;
+  int needr = 0;
+  if (a.use_b && nc > 0) {
+    int nr = (int)ceil(a.rescue_fraction * (double)nc);
+    nr = nr < nc ? nr : nc;
+    topk_reg(br, nsl, nc, nr, Tr, needr);
+  }
+
+  // union and mask emission
+  int runk = 0, runm = 0, runr = 0, count = 0;
+  const unsigned long long lt = lanemask_lt();
+  unsigned long long* mrow = a.mask + (size_t)row * a.nw;
+#pragma unroll
+  for (int e = 0; e < SPL; ++e) {
+    if (e >= nsl) continue;
+    const int j = e * 64 + l;
+    const bool c = sr.cand(e);
+    bool keep = (j == i) || (sink && j == 0 && j <= i);
+    if (a.top_k > 0) {
+      const unsigned long long tie = ballot64(c && sr.k[e] == Tk);
+      keep |= c && (sr.k[e] > Tk || ((tie >> l) & 1ull && runk + __popcll(tie & lt) < needk));
+      runk += __popcll(tie);
+    }
+    if (a.use_p) {
+      if (by_extraction) {
+        keep |= (taken >> e) & 1ull;
+      } else {
+        const unsigned long long tie = ballot64(c && sr.k[e] == Tm);
+        keep |= c && (sr.k[e] > Tm || ((tie >> l) & 1ull && runm + __popcll(tie & lt) < needm));
+        runm += __popcll(tie);
+      }
+    }
+    if (a.use_b) {
+      const unsigned long long tie = ballot64(c && br.k[e] == Tr);
+      keep |= c && (br.k[e] > Tr || ((tie >> l) & 1ull && runr + __popcll(tie & lt) < needr));
+      runr += __popcll(tie);
+    }
+    const unsigned long long word = ballot64(keep && j <= i);
+    if (l == 0) mrow[e] = word;
+    count += __popcll(word);
+  }
+  if (l == 0) {
+    a.counts[row] = count;
+    if (a.gate_out) a.gate_out[row] = fired ? 1 : 0;
+  }
+}
+
 // ------------------------------------------------------------------ CSR
 
+// row_ptr is clamped to the col_idx capacity, so a reader of the CSR can never
+// index past the buffer (the capacity bound makes the clamp a no-op).
 __global__ __launch_bounds__(1024) void scan_kernel(const int* __restrict__ counts,
-                                                    int32_t* __restrict__ row_ptr, int rows) {
+                                                    int32_t* __restrict__ row_ptr, int rows,
+                                                    int64_t capacity) {
   __shared__ int part[1024];
   const int t = threadIdx.x;
   const int chunk = (rows + 1023) / 1024;
@@ -307,12 +554,12 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int* __restrict__ coun
     part[t] += v;
     __syncthreads();
   }
-  int run = part[t] - sum;  // exclusive prefix
+  int64_t run = part[t] - sum;  // exclusive prefix
   for (int r = r0; r < r1; ++r) {
-    row_ptr[r] = run;
+    row_ptr[r] = (int32_t)(run < capacity ? run : capacity);
     run += counts[r];
   }
-  if (t == 1023) row_ptr[rows] = part[1023];
+  if (t == 1023) row_ptr[rows] = (int32_t)(part[1023] < capacity ? part[1023] : capacity);
 }
 
 __global__ __launch_bounds__(256) void compact_kernel(const unsigned long long* __restrict__ mask,
@@ -398,15 +645,31 @@ hipError_t launch_score_select(const Shape& sh, const SelectConfig& cfg, const f
   a.use_b = cfg.rescue_fraction > 0.0 ? 1 : 0;
   a.use_p = cfg.mass_threshold > 0.0f ? 1 : 0;
   a.per_wave_floats = nw * 64 * (1 + a.use_b + a.use_p);
-  const size_t per_wave_bytes = (size_t)a.per_wave_floats * sizeof(float);
-  int waves = (int)(65536 / per_wave_bytes);
-  waves = waves < 1 ? 1 : (waves > 4 ? 4 : waves);
-  hipLaunchKernelGGL(select_kernel, dim3((rows + waves - 1) / waves), dim3(64 * waves),
-                     waves * per_wave_bytes, stream, a);
+  // register form for rows up to 64*SPL = 4096 blocks, LDS form beyond
+  const int spl = nw <= 1 ? 1 : nw <= 2 ? 2 : nw <= 4 ? 4 : nw <= 8 ? 8 : nw <= 16 ? 16
+                  : nw <= 32 ? 32 : nw <= 64 ? 64 : 0;
+  const dim3 rg((rows + 3) / 4), rb(256);
+  switch (spl) {
+    case 1: hipLaunchKernelGGL(select_reg_kernel<1>, rg, rb, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL(select_reg_kernel<2>, rg, rb, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL(select_reg_kernel<4>, rg, rb, 0, stream, a); break;
+    case 8: hipLaunchKernelGGL(select_reg_kernel<8>, rg, rb, 0, stream, a); break;
+    case 16: hipLaunchKernelGGL(select_reg_kernel<16>, rg, rb, 0, stream, a); break;
+    case 32: hipLaunchKernelGGL(select_reg_kernel<32>, rg, rb, 0, stream, a); break;
+    case 64: hipLaunchKernelGGL(select_reg_kernel<64>, rg, rb, 0, stream, a); break;
+    default: {
+      const size_t per_wave_bytes = (size_t)a.per_wave_floats * sizeof(float);
+      int waves = (int)(65536 / per_wave_bytes);
+      waves = waves < 1 ? 1 : (waves > 4 ? 4 : waves);
+      hipLaunchKernelGGL(select_kernel, dim3((rows + waves - 1) / waves), dim3(64 * waves),
+                         waves * per_wave_bytes, stream, a);
+    }
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, stream, counts, row_ptr, rows);
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, stream, counts, row_ptr, rows,
+                     col_capacity);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(compact_kernel, dim3((rows + 3) / 4), dim3(256), 0, stream, mask, row_ptr,

@@ -67,6 +67,24 @@ def test_full_size_sampled_parity(cfg):
     torch.cuda.empty_cache()
 
 
+MID = [scaled(config_by_name("msa1m"), 2000 * 128 + 17, num_q_heads=4, num_kv_heads=2),
+       scaled(config_by_name("dual128k"), 4000 * 128 - 3, num_q_heads=2, num_kv_heads=1),
+       scaled(config_by_name("gated64k"), 3000 * 128, num_q_heads=2, num_kv_heads=1)]
+
+
+@pytest.mark.parametrize("cfg", MID, ids=[c.name for c in MID])
+def test_long_rows_sampled_parity(cfg):
+    """Rows of 2000-4000 candidate blocks (the selection's wider register forms)."""
+    _gpu_or_skip()
+    import bsa_check as K
+    print(f"[parity-mid] {cfg.name} S={cfg.seq_len} nb={cfg.num_blocks}", flush=True)
+    inp = generate(cfg, "cuda")
+    run = K.run_gpu(cfg, inp)
+    rep = K.check_all(cfg, inp, run, row_sample=64, unit_sample=16, score_sample=256)
+    print(f"  rows={rep.rows_checked} ambiguous={rep.ambiguous_rows} fired={rep.gate_fired} "
+          f"max_abs={rep.max_abs:.3g}", flush=True)
+
+
 def test_full_budget_equals_dense_causal():
     """k >= every candidate set: the mask is the full causal triangle, so the output is
     dense causal attention (checked against the oracle's dense routine)."""
