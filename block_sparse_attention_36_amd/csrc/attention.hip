@@ -6,25 +6,30 @@
 // "What is MSA and how does it work": the main branch attends over the
 // preselected blocks only).  Softmax is computed online, block by block.
 //
-// Work decomposition: one workgroup of four waves per (query head, query block).
-// Wave w takes query half (w & 1) and key half (w >> 1) of every kept block, so a
-// wave owns a 64-query x 64-key tile (B = 128) and keeps its own running max, sum
-// and output; the two key halves are merged once, at the end.  The score tile is
-// computed transposed, S^T = K Q^T, so that each lane holds one query column:
-// the per-query max and sum are lane-local except for a single exchange between
-// the two 32-lane halves (V_PERMLANE32_SWAP).  The probabilities then feed the
-// second product O^T = V^T P^T straight from registers as the B operand, and the
-// V^T operand is read from the row-major V tile with the gfx950 transposing LDS
-// load (DS_READ_B64_TR_B16), so V is never transposed in memory.
+// Work decomposition: one workgroup per (query head, query block), with two
+// waves per SIMD.  For B = 128 the workgroup has eight waves: wave w takes the
+// 32 queries of quarter (w % 4) and the 64 keys of half (w / 4) of every kept
+// block, keeps its own running max, sum and output, and the two key halves are
+// merged once, at the end.  The two waves that share a SIMD work on different key
+// halves, so one can run its softmax on the VALU while the other keeps the
+// matrix core busy.  The score tile is computed transposed, S^T = K Q^T, so that
+// each lane holds one query column: the per-query max and sum are lane-local
+// except for a single exchange between the two 32-lane halves
+// (V_PERMLANE32_SWAP).  The probabilities then feed the second product
+// O^T = V^T P^T straight from registers as the B operand, and the V^T operand is
+// read from the row-major V tile with the gfx950 transposing LDS load
+// (DS_READ_B64_TR_B16), so V is never transposed in memory.
 //
 // Memory: K and V tiles are double-buffered in LDS (2 x 64 KiB at D = B = 128)
-// and filled by direct global->LDS DMA one block ahead, so the next block streams
-// in while the current one is computed and no registers hold staged data.  LDS
-// rows are XOR-swizzled in 16-byte chunks so that both the 16-byte K reads (32
-// rows, one column) and the transposing V reads (4 rows, 2 chunks per 16 lanes)
-// are free of bank conflicts.  The grid is ordered by descending query block
-// (longest rows first) and maps the heads of one GQA group at one query block to
-// the same XCD, so their shared K/V blocks meet in the same L2.
+// and filled by direct global->LDS DMA.  Block n + 1 is requested right after
+// the barrier that opens block n, so it streams in while block n is computed and
+// no registers hold staged data; one barrier per block suffices.  The kept block
+// ids are read through the scalar cache one block ahead.  LDS rows are
+// XOR-swizzled in 16-byte chunks so that both the 16-byte K reads (32 rows, one
+// column) and the transposing V reads (4 rows, 2 chunks per 16 lanes) are free
+// of bank conflicts.  The grid is ordered by descending query block (longest
+// rows first) and maps the heads of one GQA group at one query block to the
+// same XCD, so their shared K/V blocks meet in the same L2.
 //
 // FP8 inputs (OCP E4M3): the raw codes are DMA'd, then expanded to bf16 in LDS
 // (exact); q_scale and k_scale fold into the per-block logit scale and v_scale
@@ -54,15 +59,15 @@ struct AttnArgs {
 
 template <int D, int B>
 struct Cfg {
-  static constexpr int QW = B / 2;       // queries per wave
-  static constexpr int KW = B / 2;       // keys per wave per block
-  static constexpr int NQT = QW / 32;    // 32-query tiles per wave
-  static constexpr int NKT = KW / 32;    // 32-key tiles per wave
-  static constexpr int NDS = D / 16;     // contraction steps of S^T = K Q^T
-  static constexpr int NDT = D / 32;     // 32-row d tiles of O^T
-  static constexpr int NKS = KW / 16;    // contraction steps of O^T = V^T P^T
-  static constexpr int ROWB = D * 2;     // bytes per bf16 LDS row
-  static constexpr int TILE = B * ROWB;  // one bf16 K or V tile in LDS
+  static constexpr int NQW = B / 32;    // 32-query groups = waves per key half
+  static constexpr int NW = 2 * NQW;    // waves per workgroup
+  static constexpr int NT = 64 * NW;    // threads per workgroup
+  static constexpr int KW = B / 2;      // keys per wave per block
+  static constexpr int NKT = KW / 32;   // 32-key tiles per wave
+  static constexpr int NDS = D / 16;    // contraction steps of S^T = K Q^T
+  static constexpr int NDT = D / 32;    // 32-row d tiles of O^T
+  static constexpr int ROWB = D * 2;    // bytes per bf16 LDS row
+  static constexpr int TILE = B * ROWB; // one bf16 K or V tile in LDS
   static constexpr int STAGE = 2 * TILE;
 };
 
@@ -127,12 +132,13 @@ template <int D, int B, bool FP8>
 struct Stage {
   typedef Cfg<D, B> C;
   static constexpr int RAW_TILE = FP8 ? B * D : C::TILE;  // bytes of K (or V) per block
-  static constexpr int NI = RAW_TILE / 4096;               // DMA instructions per wave per tile
+  static constexpr int NI = RAW_TILE / (1024 * C::NW);     // DMA instructions per wave per tile
   static constexpr int NPW = 2 * NI;                       // per wave per block
   static constexpr int RAW_STAGE = 2 * RAW_TILE;
   // raw stages [0, 2*RAW_STAGE); FP8 adds the bf16 compute stage after them
   static constexpr int LDS_BYTES = FP8 ? 2 * RAW_STAGE + C::STAGE : 2 * C::STAGE;
-  static_assert(NI >= 1 && RAW_TILE % 4096 == 0, "tile must split into 1 KiB DMAs per wave");
+  static_assert(NI >= 1 && RAW_TILE % (1024 * C::NW) == 0,
+                "tile must split into 1 KiB DMAs per wave");
 
   // Per-lane byte offsets of the NI DMA instructions inside one tile (row r of the
   // tile at r * rs, chunk swizzled for bf16), shared by K and V; computed once.
@@ -157,7 +163,7 @@ struct Stage {
   // DMA key block j of kv head g into raw stage `dst` (K tile then V tile).  Rows
   // past the ragged end re-read the last row (their logits are masked).
   static __device__ __forceinline__ void issue(const AttnArgs& a, int g, int j, unsigned char* dst,
-                                               int wave, int l, const unsigned* off) {
+                                               int wave, const unsigned* off) {
     constexpr int ES = FP8 ? 1 : 2;
     const size_t blk = ((size_t)j * B * a.Hkv + (size_t)g) * D * ES;
     const unsigned char* kb = (const unsigned char*)a.k + blk;
@@ -187,13 +193,14 @@ struct Stage {
   // FP8 only: expand the raw E4M3 tiles of `raw` into the swizzled bf16 stage.
   static __device__ __forceinline__ void expand(const unsigned char* raw, unsigned char* kt,
                                                 unsigned char* vt, int tid) {
-    constexpr int NC8 = D / 16;         // 16-code chunks per row
-    constexpr int PER = B * NC8 / 256;  // chunks per thread per tile
+    constexpr int NC8 = D / 16;             // 16-code chunks per row
+    constexpr int PER = B * NC8 / C::NT;    // chunks per thread per tile
+    static_assert(PER >= 1 && B * NC8 % C::NT == 0, "expand split");
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
       for (int n = 0; n < PER; ++n) {
-        const int ci = tid + 256 * n;
+        const int ci = tid + C::NT * n;
         const int r = ci / NC8, c = ci % NC8;
         const u32x4 w = *(const u32x4*)(raw + t * RAW_TILE + ci * 16);
 #pragma unroll
@@ -207,34 +214,29 @@ struct Stage {
   }
 };
 
-// exp2 of key tile kt2 for every query tile: p = 2^(s*sl - m), summed per query,
-// scaled by vsc (E4M3 value scale) and packed to the bf16 B operands of two steps.
-template <int D, int B>
-__device__ __forceinline__ void probs(f32x16 (&s)[B / 64][B / 64], int kt2, const float* nref,
-                                      float sl, float vsc, float* psum, u32x4 (&pk)[2][B / 64]) {
-  typedef Cfg<D, B> C;
+// exp2 of key tile kt2: p = 2^(s*sl - m), summed per query, scaled by vsc (E4M3
+// value scale) and packed to the bf16 B operands of its two 16-key steps.
+__device__ __forceinline__ void probs(const f32x16& s, float nref, float sl, float vsc, float& psum,
+                                      u32x4 (&pk)[2]) {
+  float p[16];
 #pragma unroll
-  for (int qt = 0; qt < C::NQT; ++qt) {
-    float p[16];
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      p[v] = __builtin_amdgcn_exp2f(fmaf(s[kt2][qt][v], sl, nref[qt]));
-      psum[qt] += p[v];
-    }
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        pk[sb][qt][e] = pack_bf16x2(p[8 * sb + 2 * e] * vsc, p[8 * sb + 2 * e + 1] * vsc);
+  for (int v = 0; v < 16; ++v) {
+    p[v] = __builtin_amdgcn_exp2f(fmaf(s[v], sl, nref));
+    psum += p[v];
   }
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      pk[sb][e] = pack_bf16x2(p[8 * sb + 2 * e] * vsc, p[8 * sb + 2 * e + 1] * vsc);
 }
 
 // O^T += V^T P^T over the two 16-key steps of key tile kt2.  The key rows of one
 // step are 4*hf + [0,4) (elements 0..3) and the same + 8 (elements 4..7); their
 // swizzle does not depend on the step, so the step offset folds into the read.
 template <int D, int B>
-__device__ __forceinline__ void pv_tile(const unsigned char* vrow, const u32x4 (&pk)[2][B / 64],
-                                        f32x16 (&o)[D / 32][B / 64], int kt2, int rlo, int cb0) {
+__device__ __forceinline__ void pv_tile(const unsigned char* vrow, const u32x4 (&pk)[2],
+                                        f32x16 (&o)[D / 32], int kt2, int rlo, int cb0) {
   typedef Cfg<D, B> C;
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb) {
@@ -246,22 +248,22 @@ __device__ __forceinline__ void pv_tile(const unsigned char* vrow, const u32x4 (
       const s16x4 hi = lds_read_tr16(vrow + 8 * C::ROWB + step + ((c ^ swz<D>(rlo + 8)) << 4));
       const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
       const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{lo2[0], lo2[1], hi2[0], hi2[1]});
-#pragma unroll
-      for (int qt = 0; qt < C::NQT; ++qt)
-        o[dt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            vf, __builtin_bit_cast(bf16x8, pk[sb][qt]), o[dt][qt], 0, 0, 0);
+      o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, __builtin_bit_cast(bf16x8, pk[sb]),
+                                                      o[dt], 0, 0, 0);
     }
   }
 }
 
+typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+
 template <int D, int B, bool FP8>
-__global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * 2 * (B / 32), 1) void attn_fwd_kernel(AttnArgs a) {
   typedef Cfg<D, B> C;
   typedef Stage<D, B, FP8> ST;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   const int tid = threadIdx.x, l = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int qh = wave & 1, kh = wave >> 1, hf = l >> 5;
+  const int qq = wave % C::NQW, kh = wave / C::NQW, hf = l >> 5;
 
   // ---- (head, query block) of this workgroup.  Rows are ordered kv-head major
   // (the whole chip works through one kv head's K/V at a time, a working set
@@ -280,218 +282,191 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
   const int row = unit * nb + i;
   const int e0 = a.row_ptr[row], e1 = a.row_ptr[row + 1];
   const int nblk = e1 - e0;
-  auto block_at = [&](int n) {
-    const int j = a.col_idx[e0 + n];
-    return (j >= 0 && j <= i) ? j : -1;  // -1: entry outside the causal range, skipped
-  };
+  // kept block ids through the scalar cache (read-only for the whole launch);
+  // -1 marks an entry outside the causal range, which is skipped
+  const const_i32_ptr cidx = (const_i32_ptr)a.col_idx + e0;
+  auto valid = [&](int j) { return (j >= 0 && j <= i) ? j : -1; };
   unsigned doff[ST::NI];
   ST::plan(a, wave, l, doff);
+  // block n + 1's id is loaded during block n - 1 and first used in block n, so
+  // the scalar load never stalls the loop
+  int jcur = -1, jraw = -1;
   if (nblk > 0) {
-    const int j0 = block_at(0);
-    ST::issue(a, g, j0 < 0 ? 0 : j0, lds, wave, l, doff);
+    jcur = valid(cidx[0]);
+    ST::issue(a, g, jcur < 0 ? 0 : jcur, lds, wave, doff);
+    if (nblk > 1) jraw = cidx[1];
   }
 
   // ---- Q fragments (B operand of S^T = K Q^T): query column = lane % 32,
   // contraction index d = ds*16 + hf*8 + [0, 8)
-  bf16x8 qf[C::NQT][C::NDS];
+  bf16x8 qf[C::NDS];
   const float qsc = FP8 ? a.q_scale[(size_t)h * nb + i] : 1.0f;
-#pragma unroll
-  for (int qt = 0; qt < C::NQT; ++qt) {
+  const int qi = qq * 32 + (l & 31);  // this lane's query inside the block
+  {
     // rows past the ragged end load the last row instead (their outputs are not stored)
-    int64_t t = (int64_t)i * B + qh * C::QW + qt * 32 + (l & 31);
+    int64_t t = (int64_t)i * B + qi;
     t = t < a.S ? t : a.S - 1;
 #pragma unroll
     for (int ds = 0; ds < C::NDS; ++ds) {
       const size_t off = ((size_t)t * a.Hq + h) * D + ds * 16 + hf * 8;
       if (!FP8) {
-        qf[qt][ds] = __builtin_bit_cast(bf16x8, *(const u32x4*)((const uint16_t*)a.q + off));
+        qf[ds] = __builtin_bit_cast(bf16x8, *(const u32x4*)((const uint16_t*)a.q + off));
       } else {
         const u32x2 raw = *(const u32x2*)((const uint8_t*)a.q + off);
         const u32x2 lo = e4m3x4_to_bf16x4(raw[0]), hi = e4m3x4_to_bf16x4(raw[1]);
-        qf[qt][ds] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+        qf[ds] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
       }
     }
   }
 
-  f32x16 o[C::NDT][C::NQT];
-  float m[C::NQT], lsum[C::NQT];
+  f32x16 o[C::NDT];
+  float m = -INFINITY, lsum = 0.f;
 #pragma unroll
-  for (int qt = 0; qt < C::NQT; ++qt) {
-    m[qt] = -INFINITY;
-    lsum[qt] = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < C::NDT; ++dt) o[dt][qt] = f32x16{0};
-  }
+  for (int dt = 0; dt < C::NDT; ++dt) o[dt] = f32x16{0};
+
+  const int krow0 = (kh * C::KW + (l & 31)) * C::ROWB;
+  const int kx = hf ^ swz<D>(l & 31);
+  const int rlo = 4 * hf + ((l & 15) >> 2);                  // row within a 16-key step
+  const int cb0 = (((l >> 4) & 1) * 16 + 4 * (l & 3)) * 2;  // byte column in a d tile
+  const int kfirst = kh * C::KW + hf * 4;                    // first key row of this lane
 
   for (int n = 0; n < nblk; ++n) {
-    const int j = block_at(n);
-    unsigned char* raw = lds + (n & 1) * ST::RAW_STAGE;
-    if (n + 1 < nblk) {
-      const int jn = block_at(n + 1);
-      ST::issue(a, g, jn < 0 ? 0 : jn, lds + ((n + 1) & 1) * ST::RAW_STAGE, wave, l, doff);
-      wait_vmcnt<ST::NPW>();  // this wave's DMAs of block n have landed
-    } else {
-      wait_vmcnt<0>();
-    }
-    lds_barrier();  // ... and every other wave's
-    unsigned char* kt = raw;
+    const int j = jcur;
+    wait_vmcnt<0>();  // this wave's share of block n has landed
+    lds_barrier();    // ... and every other wave's; all are done with block n - 1
+    const int jn = valid(jraw);
+    if (n + 1 < nblk)
+      ST::issue(a, g, jn < 0 ? 0 : jn, lds + ((n + 1) & 1) * ST::RAW_STAGE, wave, doff);
+    jcur = jn;
+    jraw = n + 2 < nblk ? cidx[n + 2] : -1;
+    unsigned char* kt = lds + (n & 1) * ST::RAW_STAGE;
     if (FP8) {
       kt = lds + 2 * ST::RAW_STAGE;
-      ST::expand(raw, kt, kt + C::TILE, tid);
+      ST::expand(lds + (n & 1) * ST::RAW_STAGE, kt, kt + C::TILE, tid);
       lds_barrier();
     }
-    unsigned char* vt = kt + C::TILE;
+    const unsigned char* vt = kt + C::TILE;
+    if (j < 0) continue;
 
-    if (j >= 0) {
-      // ---- S^T = K Q^T: A = K rows (keys), B = Q columns (queries).
-      // Row kh*KW + kt2*32 + (l&31) has the same swizzle for every kt2 (it depends
-      // on the row's low 4 bits only), so one lane address per contraction step
-      // serves both key tiles, the tile offset folding into the instruction.
-      f32x16 s[C::NKT][C::NQT];
+    // ---- S^T = K Q^T: A = K rows (keys), B = Q columns (queries).
+    // Row kh*KW + kt2*32 + (l&31) has the same swizzle for every kt2 (it depends
+    // on the row's low 4 bits only), so one lane address per contraction step
+    // serves every key tile, the tile offset folding into the instruction.
+    f32x16 s[C::NKT];
+#pragma unroll
+    for (int kt2 = 0; kt2 < C::NKT; ++kt2) s[kt2] = f32x16{0};
+    const unsigned char* krow = kt + krow0;
+#pragma unroll
+    for (int ds = 0; ds < C::NDS; ++ds) {
+      const unsigned char* ka = krow + (((2 * ds) ^ kx) << 4);
+#pragma unroll
+      for (int kt2 = 0; kt2 < C::NKT; ++kt2) {
+        const bf16x8 kf = *(const bf16x8*)(ka + kt2 * 32 * C::ROWB);
+        s[kt2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ds], s[kt2], 0, 0, 0);
+      }
+    }
+
+    // ---- online softmax (log2 domain); lane = one query, registers = keys.
+    // The running reference max only moves when the block max exceeds it by
+    // more than 8 (a factor 256), so the output rescale is rare; every
+    // probability stays below 2^8 and the result is the same up to rounding.
+    const float sl = a.scale_log2 * (FP8 ? qsc * a.k_scale[(size_t)g * nb + j] : 1.0f);
+    const float vsc = FP8 ? a.v_scale[(size_t)g * nb + j] : 1.0f;
+    float mx = -INFINITY;
+    // causal mask on the diagonal block and the ragged tail: key (kt2, v) of this
+    // lane sits at offset kw = kt2*32 + (v>>2)*8 + (v&3) from the lane's first
+    // key; it is masked when kw exceeds a per-lane limit (block-dependent, so the
+    // comparisons stay inside the loop and only run on those blocks)
+    if ((j == i) || ((int64_t)j * B + kh * C::KW + C::KW > a.S)) {
+      const int64_t left = a.S - (int64_t)j * B - 1 - kfirst;  // last valid kw
+      int lim = (int)(left < 4 * B ? left : 4 * B);
+      if (j == i) lim = min(lim, qi - kfirst);
 #pragma unroll
       for (int kt2 = 0; kt2 < C::NKT; ++kt2)
 #pragma unroll
-        for (int qt = 0; qt < C::NQT; ++qt) s[kt2][qt] = f32x16{0};
-      const unsigned char* krow = kt + (kh * C::KW + (l & 31)) * C::ROWB;
-      const int kx = hf ^ swz<D>(l & 31);
-#pragma unroll
-      for (int ds = 0; ds < C::NDS; ++ds) {
-        const unsigned char* ka = krow + (((2 * ds) ^ kx) << 4);
-#pragma unroll
-        for (int kt2 = 0; kt2 < C::NKT; ++kt2) {
-          const bf16x8 kf = *(const bf16x8*)(ka + kt2 * 32 * C::ROWB);
-#pragma unroll
-          for (int qt = 0; qt < C::NQT; ++qt)
-            s[kt2][qt] =
-                __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qt][ds], s[kt2][qt], 0, 0, 0);
+        for (int v = 0; v < 16; ++v) {
+          const int kw = kt2 * 32 + (v >> 2) * 8 + (v & 3);
+          const float x = kw > lim ? -INFINITY : s[kt2][v];
+          s[kt2][v] = x;
+          mx = fmaxf(mx, x);
         }
-      }
-
-      // ---- online softmax (log2 domain); lane = one query, registers = keys.
-      // The running reference max only moves when the block max exceeds it by
-      // more than 8 (a factor 256), so the output rescale is rare; every
-      // probability stays below 2^8 and the result is the same up to rounding.
-      const float sl = a.scale_log2 * (FP8 ? qsc * a.k_scale[(size_t)g * nb + j] : 1.0f);
-      const float vsc = FP8 ? a.v_scale[(size_t)g * nb + j] : 1.0f;
-      // causal mask on the diagonal block and the ragged tail: key (kt2, v) of this
-      // lane sits at offset kw = kt2*32 + (v>>2)*8 + (v&3) from the lane's first
-      // key; it is masked when kw exceeds a per-lane limit (block-dependent, so
-      // the comparisons stay inside the loop and only run on those blocks)
-      const bool masked = (j == i) || ((int64_t)j * B + kh * C::KW + C::KW > a.S);
-      const int kfirst = kh * C::KW + hf * 4;
-      const int64_t left = a.S - (int64_t)j * B - 1 - kfirst;  // last valid kw
-      float nref[C::NQT];
+    } else {
 #pragma unroll
-      for (int qt = 0; qt < C::NQT; ++qt) {
-        // block max on the raw scores (sl > 0), then one FMA + exp2 per element
-        float mx = -INFINITY;
-        if (masked) {
-          const int qi = qh * C::QW + qt * 32 + (l & 31);  // query index in the block
-          int lim = (int)(left < 4 * B ? left : 4 * B);
-          if (j == i) lim = min(lim, qi - kfirst);
+      for (int kt2 = 0; kt2 < C::NKT; ++kt2)
 #pragma unroll
-          for (int kt2 = 0; kt2 < C::NKT; ++kt2)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              const int kw = kt2 * 32 + (v >> 2) * 8 + (v & 3);
-              const float x = kw > lim ? -INFINITY : s[kt2][qt][v];
-              s[kt2][qt][v] = x;
-              mx = fmaxf(mx, x);
-            }
-        } else {
-#pragma unroll
-          for (int kt2 = 0; kt2 < C::NKT; ++kt2)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kt2][qt][v]);
-        }
-        mx = max_with_other_half(mx) * sl;
-        const bool bump = mx > m[qt] + 8.0f;  // also true for the first finite block max
-        if (__ballot(bump)) {
-          // lanes that do not move keep alpha = 1 (their max may still be -inf)
-          const float alpha = bump ? __builtin_amdgcn_exp2f(m[qt] - mx) : 1.0f;  // 0 from -inf
-          m[qt] = bump ? mx : m[qt];
-          lsum[qt] *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < C::NDT; ++dt)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) o[dt][qt][v] *= alpha;
-        }
-        nref[qt] = m[qt] == -INFINITY ? 0.f : -m[qt];
-      }
-
-      // ---- exp2 + bf16 packing of key tile 0, then O^T += V^T P^T for tile 0 while
-      // the VALU turns key tile 1 into probabilities (independent work, same block)
-      float psum[C::NQT];
-#pragma unroll
-      for (int qt = 0; qt < C::NQT; ++qt) psum[qt] = 0.f;
-      const int rlo = 4 * hf + ((l & 15) >> 2);  // row within a 16-key step
-      const int cb0 = (((l >> 4) & 1) * 16 + 4 * (l & 3)) * 2;  // byte column in a d tile
-      const unsigned char* vrow = vt + (kh * C::KW + rlo) * C::ROWB + (cb0 & 15);
-      u32x4 pk0[2][C::NQT], pk1[2][C::NQT];
-      probs<D, B>(s, 0, nref, sl, vsc, psum, pk0);
-      pv_tile<D, B>(vrow, pk0, o, 0, rlo, cb0);
-      if (C::NKT > 1) {
-        probs<D, B>(s, C::NKT - 1, nref, sl, vsc, psum, pk1);
-        pv_tile<D, B>(vrow, pk1, o, C::NKT - 1, rlo, cb0);
-      }
-#pragma unroll
-      for (int qt = 0; qt < C::NQT; ++qt) lsum[qt] += psum[qt];
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kt2][v]);
     }
-    lds_barrier();  // every wave is done with this stage before it is refilled
+    // block max on the raw scores (sl > 0), then one FMA + exp2 per element
+    mx = max_with_other_half(mx) * sl;
+    const bool bump = mx > m + 8.0f;  // also true for the first finite block max
+    if (__ballot(bump)) {
+      // lanes that do not move keep alpha = 1 (their max may still be -inf)
+      const float alpha = bump ? __builtin_amdgcn_exp2f(m - mx) : 1.0f;  // 0 from -inf
+      m = bump ? mx : m;
+      lsum *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[dt][v] *= alpha;
+    }
+    const float nref = m == -INFINITY ? 0.f : -m;
+
+    // ---- exp2 + bf16 packing per key tile, each followed by O^T += V^T P^T for
+    // that tile (the next tile's exp2 is independent of this tile's products)
+    float psum = 0.f;
+    const unsigned char* vrow = vt + (kh * C::KW + rlo) * C::ROWB + (cb0 & 15);
+#pragma unroll
+    for (int kt2 = 0; kt2 < C::NKT; ++kt2) {
+      u32x4 pk[2];
+      probs(s[kt2], nref, sl, vsc, psum, pk);
+      pv_tile<D, B>(vrow, pk, o, kt2, rlo, cb0);
+    }
+    lsum += psum;
   }
 
   // ---- merge the two key halves: lanes first (sum of the halves' partial sums),
   // then waves kh = 1 hand their state to kh = 0 through LDS
-#pragma unroll
-  for (int qt = 0; qt < C::NQT; ++qt) lsum[qt] += other_half(lsum[qt]);
-  float* xo = (float*)lds + (size_t)qh * (C::NDT * C::NQT * 16 * 64 + 2 * C::NQT * 64);
-  float* xm = xo + C::NDT * C::NQT * 16 * 64;
-  float* xl = xm + C::NQT * 64;
+  lsum += other_half(lsum);
+  lds_barrier();  // every wave is done with the last stage before it is reused
+  float* xo = (float*)lds + (size_t)qq * (C::NDT * 16 * 64 + 2 * 64);
+  float* xm = xo + C::NDT * 16 * 64;
+  float* xl = xm + 64;
   if (kh == 1) {
 #pragma unroll
     for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
-      for (int qt = 0; qt < C::NQT; ++qt)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) xo[((dt * C::NQT + qt) * 16 + v) * 64 + l] = o[dt][qt][v];
-#pragma unroll
-    for (int qt = 0; qt < C::NQT; ++qt) {
-      xm[qt * 64 + l] = m[qt];
-      xl[qt * 64 + l] = lsum[qt];
-    }
+      for (int v = 0; v < 16; ++v) xo[(dt * 16 + v) * 64 + l] = o[dt][v];
+    xm[l] = m;
+    xl[l] = lsum;
   }
   lds_barrier();
   if (kh == 1) return;
 
   uint16_t* out = (uint16_t*)a.out;
+  const float m1 = xm[l], l1 = xl[l];
+  const float mt = fmaxf(m, m1);
+  const float mref = mt == -INFINITY ? 0.f : mt;
+  const float a0 = exp2f(m - mref), a1 = exp2f(m1 - mref);
+  const float lt = lsum * a0 + l1 * a1;
+  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+  const int64_t t = (int64_t)i * B + qi;
+  if (t < a.S) {
+    uint16_t* orow = out + ((size_t)t * a.Hq + h) * D;
 #pragma unroll
-  for (int qt = 0; qt < C::NQT; ++qt) {
-    const float m1 = xm[qt * 64 + l], l1 = xl[qt * 64 + l];
-    const float mt = fmaxf(m[qt], m1);
-    const float mref = mt == -INFINITY ? 0.f : mt;
-    const float a0 = exp2f(m[qt] - mref), a1 = exp2f(m1 - mref);
-    const float lt = lsum[qt] * a0 + l1 * a1;
-    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-    const int qi = qh * C::QW + qt * 32 + (l & 31);
-    const int64_t t = (int64_t)i * B + qi;
-    if (t < a.S) {
-      uint16_t* orow = out + ((size_t)t * a.Hq + h) * D;
+    for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
-      for (int dt = 0; dt < C::NDT; ++dt)
+      for (int vg = 0; vg < 4; ++vg) {
+        float y[4];
 #pragma unroll
-        for (int vg = 0; vg < 4; ++vg) {
-          float y[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int v = vg * 4 + e;
-            y[e] = (o[dt][qt][v] * a0 + xo[((dt * C::NQT + qt) * 16 + v) * 64 + l] * a1) * inv;
-          }
-          const int d = dt * 32 + vg * 8 + hf * 4;
-          *(u32x2*)(orow + d) = u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+        for (int e = 0; e < 4; ++e) {
+          const int v = vg * 4 + e;
+          y[e] = (o[dt][v] * a0 + xo[(dt * 16 + v) * 64 + l] * a1) * inv;
         }
-      if (a.lse && hf == 0)
-        a.lse[(size_t)h * a.S + t] = lt > 0.f ? (mt + log2f(lt)) * kLn2 : -INFINITY;
-    }
+        const int d = dt * 32 + vg * 8 + hf * 4;
+        *(u32x2*)(orow + d) = u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+      }
+    if (a.lse && hf == 0)
+      a.lse[(size_t)h * a.S + t] = lt > 0.f ? (mt + log2f(lt)) * kLn2 : -INFINITY;
   }
 }
 
@@ -507,7 +482,8 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
                               hipFuncAttributeMaxDynamicSharedMemorySize, ST::LDS_BYTES);
     attr_set = true;
   }
-  hipLaunchKernelGGL((attn_fwd_kernel<D, B, FP8>), dim3(rows8 * 8 * G), dim3(256), ST::LDS_BYTES,
+  hipLaunchKernelGGL((attn_fwd_kernel<D, B, FP8>), dim3(rows8 * 8 * G), dim3(Cfg<D, B>::NT),
+                     ST::LDS_BYTES,
                      stream, a);
   return hipGetLastError();
 }
