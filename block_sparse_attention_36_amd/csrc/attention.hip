@@ -24,7 +24,7 @@
 // and filled by direct global->LDS DMA.  Block n + 1 is requested right after
 // the barrier that opens block n, so it streams in while block n is computed and
 // no registers hold staged data; one barrier per block suffices.  The kept block
-// ids are read through the scalar cache one block ahead.  LDS rows are
+// ids are read one block ahead.  LDS rows are
 // XOR-swizzled in 16-byte chunks so that both the 16-byte K reads (32 rows, one
 // column) and the transposing V reads (4 rows, 2 chunks per 16 lanes) are free
 // of bank conflicts.  The grid is ordered by descending query block (longest
@@ -115,16 +115,23 @@ __device__ __forceinline__ void dma16(const void* sbase, unsigned voff, unsigned
 }
 #pragma clang diagnostic pop
 
-// Wait until at most N vector-memory operations of this wave are outstanding.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+// Wait until no vector-memory operation of this wave is outstanding.  This is
+// the S_WAITCNT builtin (vmcnt 0, expcnt and lgkmcnt left open) rather than
+// inline asm, so the compiler sees the wait and knows every earlier vector load
+// has completed; otherwise it keeps ordinary loads issued before the loop (the
+// Q fragments) pending and waits on vmcnt inside the loop, which, counting the
+// DMAs it cannot see, would stall on the next block's transfer.
+__device__ __forceinline__ void wait_vmem_all() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // gfx9 encoding: vmcnt(0) expcnt(7) lgkmcnt(15)
 }
 
-// Workgroup barrier that also completes this wave's LDS accesses; the memory
-// clobber keeps the compiler from moving loads or stores across it.
+// Workgroup barrier that also completes this wave's LDS accesses.  The builtin
+// wait tells the compiler that nothing counted by lgkmcnt is outstanding (a
+// pending scalar load would otherwise force every later LDS wait down to zero);
+// the asm repeats it next to the barrier, and its memory clobber keeps the
+// compiler from moving loads or stores across.
 __device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // gfx9 encoding: vmcnt(63) expcnt(7) lgkmcnt(0)
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
@@ -133,7 +140,6 @@ struct Stage {
   typedef Cfg<D, B> C;
   static constexpr int RAW_TILE = FP8 ? B * D : C::TILE;  // bytes of K (or V) per block
   static constexpr int NI = RAW_TILE / (1024 * C::NW);     // DMA instructions per wave per tile
-  static constexpr int NPW = 2 * NI;                       // per wave per block
   static constexpr int RAW_STAGE = 2 * RAW_TILE;
   // raw stages [0, 2*RAW_STAGE); FP8 adds the bf16 compute stage after them
   static constexpr int LDS_BYTES = FP8 ? 2 * RAW_STAGE + C::STAGE : 2 * C::STAGE;
@@ -254,8 +260,6 @@ __device__ __forceinline__ void pv_tile(const unsigned char* vrow, const u32x4 (
   }
 }
 
-typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
-
 template <int D, int B, bool FP8>
 __global__ __launch_bounds__(64 * 2 * (B / 32), 1) void attn_fwd_kernel(AttnArgs a) {
   typedef Cfg<D, B> C;
@@ -282,18 +286,26 @@ __global__ __launch_bounds__(64 * 2 * (B / 32), 1) void attn_fwd_kernel(AttnArgs
   const int row = unit * nb + i;
   const int e0 = a.row_ptr[row], e1 = a.row_ptr[row + 1];
   const int nblk = e1 - e0;
-  // kept block ids through the scalar cache (read-only for the whole launch);
   // -1 marks an entry outside the causal range, which is skipped
-  const const_i32_ptr cidx = (const_i32_ptr)a.col_idx + e0;
+  const int32_t* cidx = a.col_idx + e0;
   auto valid = [&](int j) { return (j >= 0 && j <= i) ? j : -1; };
   unsigned doff[ST::NI];
   ST::plan(a, wave, l, doff);
-  // block n + 1's id is loaded during block n - 1 and first used in block n, so
-  // the scalar load never stalls the loop
+  // Per-block values are fetched one block ahead with ordinary vector loads
+  // issued right after the loop's vmcnt(0) wait: block n + 1's id is loaded
+  // during block n - 1 and its E4M3 scales during block n, and each is first
+  // used after the next such wait, so neither ever stalls the loop.  (Scalar
+  // loads would share lgkmcnt with the LDS reads and, returning out of order,
+  // force every LDS wait down to zero.)
   int jcur = -1, jraw = -1;
+  float kscur = 1.0f, vscur = 1.0f;
   if (nblk > 0) {
-    jcur = valid(cidx[0]);
+    jcur = valid(__builtin_amdgcn_readfirstlane(cidx[0]));
     ST::issue(a, g, jcur < 0 ? 0 : jcur, lds, wave, doff);
+    if (FP8) {
+      kscur = a.k_scale[(size_t)g * nb + (jcur < 0 ? 0 : jcur)];
+      vscur = a.v_scale[(size_t)g * nb + (jcur < 0 ? 0 : jcur)];
+    }
     if (nblk > 1) jraw = cidx[1];
   }
 
@@ -332,11 +344,17 @@ __global__ __launch_bounds__(64 * 2 * (B / 32), 1) void attn_fwd_kernel(AttnArgs
 
   for (int n = 0; n < nblk; ++n) {
     const int j = jcur;
-    wait_vmcnt<0>();  // this wave's share of block n has landed
+    const float ksc = kscur, vsc = vscur;
+    wait_vmem_all();  // this wave's share of block n has landed
     lds_barrier();    // ... and every other wave's; all are done with block n - 1
-    const int jn = valid(jraw);
-    if (n + 1 < nblk)
+    const int jn = valid(__builtin_amdgcn_readfirstlane(jraw));
+    if (n + 1 < nblk) {
       ST::issue(a, g, jn < 0 ? 0 : jn, lds + ((n + 1) & 1) * ST::RAW_STAGE, wave, doff);
+      if (FP8) {
+        kscur = a.k_scale[(size_t)g * nb + (jn < 0 ? 0 : jn)];
+        vscur = a.v_scale[(size_t)g * nb + (jn < 0 ? 0 : jn)];
+      }
+    }
     jcur = jn;
     jraw = n + 2 < nblk ? cidx[n + 2] : -1;
     unsigned char* kt = lds + (n & 1) * ST::RAW_STAGE;
@@ -351,27 +369,34 @@ __global__ __launch_bounds__(64 * 2 * (B / 32), 1) void attn_fwd_kernel(AttnArgs
     // ---- S^T = K Q^T: A = K rows (keys), B = Q columns (queries).
     // Row kh*KW + kt2*32 + (l&31) has the same swizzle for every kt2 (it depends
     // on the row's low 4 bits only), so one lane address per contraction step
-    // serves every key tile, the tile offset folding into the instruction.
+    // serves every key tile, the tile offset folding into the instruction.  All
+    // K fragments are requested before the first product (the scheduling
+    // barrier keeps the compiler from sinking each read onto its MFMA), so the
+    // products consume them as they arrive instead of waiting on each read.
     f32x16 s[C::NKT];
 #pragma unroll
     for (int kt2 = 0; kt2 < C::NKT; ++kt2) s[kt2] = f32x16{0};
     const unsigned char* krow = kt + krow0;
+    bf16x8 kf[C::NDS][C::NKT];
 #pragma unroll
     for (int ds = 0; ds < C::NDS; ++ds) {
       const unsigned char* ka = krow + (((2 * ds) ^ kx) << 4);
 #pragma unroll
-      for (int kt2 = 0; kt2 < C::NKT; ++kt2) {
-        const bf16x8 kf = *(const bf16x8*)(ka + kt2 * 32 * C::ROWB);
-        s[kt2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ds], s[kt2], 0, 0, 0);
-      }
+      for (int kt2 = 0; kt2 < C::NKT; ++kt2)
+        kf[ds][kt2] = *(const bf16x8*)(ka + kt2 * 32 * C::ROWB);
     }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ds = 0; ds < C::NDS; ++ds)
+#pragma unroll
+      for (int kt2 = 0; kt2 < C::NKT; ++kt2)
+        s[kt2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ds][kt2], qf[ds], s[kt2], 0, 0, 0);
 
     // ---- online softmax (log2 domain); lane = one query, registers = keys.
     // The running reference max only moves when the block max exceeds it by
     // more than 8 (a factor 256), so the output rescale is rare; every
     // probability stays below 2^8 and the result is the same up to rounding.
-    const float sl = a.scale_log2 * (FP8 ? qsc * a.k_scale[(size_t)g * nb + j] : 1.0f);
-    const float vsc = FP8 ? a.v_scale[(size_t)g * nb + j] : 1.0f;
+    const float sl = a.scale_log2 * (FP8 ? qsc * ksc : 1.0f);
     float mx = -INFINITY;
     // causal mask on the diagonal block and the ragged tail: key (kt2, v) of this
     // lane sits at offset kw = kt2*32 + (v>>2)*8 + (v&3) from the lane's first
