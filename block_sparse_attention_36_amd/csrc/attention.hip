@@ -26,7 +26,7 @@
 // no registers hold staged data; one barrier per block suffices.  The kept block
 // ids are read one block ahead.  LDS rows are
 // XOR-swizzled in 16-byte chunks so that both the 16-byte K reads (32 rows, one
-// column) and the transposing V reads (4 rows, 2 chunks per 16 lanes) are free
+// column) and the transposing V reads (4 rows x 4 chunks per 32 lanes) are free
 // of bank conflicts.  The grid is ordered by descending query block (longest
 // rows first) and maps the heads of one GQA group at one query block to the
 // same XCD, so their shared K/V blocks meet in the same L2.
@@ -72,12 +72,17 @@ struct Cfg {
 };
 
 // XOR applied to the 16-byte chunk index of LDS row r, shared by the K and V
-// tiles.  It places the 16 rows of one chunk column (the K operand reads) and
-// the 4 rows x 2 chunks of one transposing V read on distinct 16-byte slots of a
-// 256-byte bank window, so neither access pattern has bank conflicts.
+// tiles; it depends on r mod 16 only.  D = 128 (256-byte rows, 16 chunks): the
+// 16 rows of one chunk column (the 16-byte K operand reads) land on 16 distinct
+// chunks of the 256-byte bank window, and any 4 consecutive rows are moved to
+// 4 different 4-chunk groups, so a transposing V read (4 rows x 4 chunks over
+// 32 lanes) touches every bank once.  D = 64 (128-byte rows, two per window):
+// the same two properties among the rows of one parity.
 template <int D>
 __device__ __forceinline__ int swz(int r) {
-  return D == 128 ? (((r & 7) << 1) | ((r >> 3) & 1)) : ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
+  if (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  const int k = (r >> 1) & 7;
+  return ((k & 1) << 2) | (k >> 1);
 }
 template <int D>
 __device__ __forceinline__ int k_off(int r, int c) {
