@@ -144,12 +144,15 @@ template <int D, int B, bool FP8>
 struct Stage {
   typedef Cfg<D, B> C;
   static constexpr int RAW_TILE = FP8 ? B * D : C::TILE;  // bytes of K (or V) per block
-  static constexpr int NI = RAW_TILE / (1024 * C::NW);     // DMA instructions per wave per tile
+  // DMA instructions per issuing wave per tile: only the waves of key half 0
+  // request tiles, so that the half-1 waves sharing their SIMDs start on the
+  // products while the texture-address queue drains
+  static constexpr int NI = 2 * RAW_TILE / (1024 * C::NW);
   static constexpr int RAW_STAGE = 2 * RAW_TILE;
   // raw stages [0, 2*RAW_STAGE); FP8 adds the bf16 compute stage after them
   static constexpr int LDS_BYTES = FP8 ? 2 * RAW_STAGE + C::STAGE : 2 * C::STAGE;
-  static_assert(NI >= 1 && RAW_TILE % (1024 * C::NW) == 0,
-                "tile must split into 1 KiB DMAs per wave");
+  static_assert(NI >= 1 && 2 * RAW_TILE % (1024 * C::NW) == 0,
+                "tile must split into 1 KiB DMAs per issuing wave");
 
   // Per-lane byte offsets of the NI DMA instructions inside one tile (row r of the
   // tile at r * rs, chunk swizzled for bf16), shared by K and V; computed once.
@@ -158,7 +161,7 @@ struct Stage {
     const unsigned rs = (unsigned)(a.Hkv * D * ES);
 #pragma unroll
     for (int n = 0; n < NI; ++n) {
-      const int p = (wave * NI + n) * 1024 + 16 * l;
+      const int p = ((wave % C::NQW) * NI + n) * 1024 + 16 * l;
       int r, col;  // tile row and byte column of this lane's 16 bytes
       if (!FP8) {
         r = p / C::ROWB;
@@ -171,10 +174,12 @@ struct Stage {
     }
   }
 
-  // DMA key block j of kv head g into raw stage `dst` (K tile then V tile).  Rows
-  // past the ragged end re-read the last row (their logits are masked).
+  // DMA key block j of kv head g into raw stage `dst` (K tile then V tile); a
+  // no-op for the waves of key half 1.  Rows past the ragged end re-read the
+  // last row (their logits are masked).
   static __device__ __forceinline__ void issue(const AttnArgs& a, int g, int j, unsigned char* dst,
                                                int wave, const unsigned* off) {
+    if (wave >= C::NQW) return;
     constexpr int ES = FP8 ? 1 : 2;
     const size_t blk = ((size_t)j * B * a.Hkv + (size_t)g) * D * ES;
     const unsigned char* kb = (const unsigned char*)a.k + blk;
@@ -183,7 +188,7 @@ struct Stage {
     if (left >= B) {
 #pragma unroll
       for (int n = 0; n < NI; ++n) {
-        const int base = (wave * NI + n) * 1024;
+        const int base = ((wave % C::NQW) * NI + n) * 1024;
         dma16(kb, off[n], lds_addr(dst + base));
         dma16(vb, off[n], lds_addr(dst + RAW_TILE + base));
       }
@@ -192,7 +197,7 @@ struct Stage {
       const unsigned last = (unsigned)(left - 1) * rs;  // ragged block: clamp the row
 #pragma unroll
       for (int n = 0; n < NI; ++n) {
-        const int base = (wave * NI + n) * 1024;
+        const int base = ((wave % C::NQW) * NI + n) * 1024;
         const unsigned col = off[n] % rs, rowoff = off[n] - col;
         const unsigned o = (rowoff < last ? rowoff : last) + col;
         dma16(kb, o, lds_addr(dst + base));
@@ -458,6 +463,7 @@ __global__ __launch_bounds__(64 * 2 * (B / 32), 1) void attn_fwd_kernel(AttnArgs
   // then waves kh = 1 hand their state to kh = 0 through LDS
   lsum += other_half(lsum);
   lds_barrier();  // every wave is done with the last stage before it is reused
+  // O moves in 16-byte pieces: piece (dt, vg) of lane l at ((dt*4 + vg)*64 + l)*16
   float* xo = (float*)lds + (size_t)qq * (C::NDT * 16 * 64 + 2 * 64);
   float* xm = xo + C::NDT * 16 * 64;
   float* xl = xm + 64;
@@ -465,7 +471,9 @@ __global__ __launch_bounds__(64 * 2 * (B / 32), 1) void attn_fwd_kernel(AttnArgs
 #pragma unroll
     for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) xo[(dt * 16 + v) * 64 + l] = o[dt][v];
+      for (int vg = 0; vg < 4; ++vg)
+        *(f32x4*)(xo + ((dt * 4 + vg) * 64 + l) * 4) =
+            f32x4{o[dt][4 * vg], o[dt][4 * vg + 1], o[dt][4 * vg + 2], o[dt][4 * vg + 3]};
     xm[l] = m;
     xl[l] = lsum;
   }
@@ -486,12 +494,10 @@ __global__ __launch_bounds__(64 * 2 * (B / 32), 1) void attn_fwd_kernel(AttnArgs
     for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
       for (int vg = 0; vg < 4; ++vg) {
+        const f32x4 x1 = *(const f32x4*)(xo + ((dt * 4 + vg) * 64 + l) * 4);
         float y[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int v = vg * 4 + e;
-          y[e] = (o[dt][v] * a0 + xo[(dt * 16 + v) * 64 + l] * a1) * inv;
-        }
+        for (int e = 0; e < 4; ++e) y[e] = (o[dt][vg * 4 + e] * a0 + x1[e] * a1) * inv;
         const int d = dt * 32 + vg * 8 + hf * 4;
         *(u32x2*)(orow + d) = u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
       }
