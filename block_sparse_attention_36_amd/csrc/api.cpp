@@ -195,6 +195,8 @@ bsa_status bsa_score_select(const bsa_problem* problem, const bsa_select_params*
   if (sh.S == 0) return ok();
   if (!q_centroid || !k_centroid || !row_ptr || !col_idx)
     return fail(BSA_ERR_INVALID_ARGUMENT, "q_centroid, k_centroid, row_ptr and col_idx are required");
+  if (((uintptr_t)q_centroid | (uintptr_t)k_centroid | (uintptr_t)row_ptr | (uintptr_t)workspace) & 15)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "q_centroid, k_centroid, row_ptr and workspace must be 16-byte aligned");
   const bool rescue = params->rescue_fraction > 0.0;
   if (rescue && (!q_norm || !k_radius))
     return fail(BSA_ERR_INVALID_ARGUMENT, "the rescue branch needs q_norm and k_radius");

@@ -6,11 +6,12 @@
 // per-(prompt, layer, head) key-block radius (RBS-Attention, third and fourth
 // paragraphs), here the largest distance of a key from its block mean.
 //
-// Design: HBM-bound streaming reduction.  One workgroup per (token block, chunk of
-// heads); each thread owns 8 consecutive elements of the [H*D] token row, so every
-// row load is one contiguous, fully coalesced 16-byte (bf16) or 8-byte (E4M3)
-// access per thread, and the reduction over the block's rows stays in registers.
-// Rows are loaded eight at a time to keep enough bytes in flight per thread.
+// Design: HBM-bound streaming reduction.  Each thread owns 8 consecutive elements
+// of the [H*D] token row, so every row load is one contiguous, fully coalesced
+// 16-byte (bf16) or 8-byte (E4M3) access per thread.  Queries: one workgroup per
+// (token block, chunk of heads), rows loaded eight at a time.  Keys (far fewer
+// heads): eight waves per block split its rows, which stay in registers for the
+// radius pass.
 #include "common.h"
 #include "launch.h"
 
@@ -157,58 +158,87 @@ __global__ void pool_q_kernel(const void* __restrict__ q, const float* __restric
   }
 }
 
-template <bool FP8, int D>
-__global__ void pool_k_kernel(const void* __restrict__ k, const float* __restrict__ k_scale,
-                              float* __restrict__ kc, float* __restrict__ kr, int64_t S, int Hkv,
-                              int B, int nb, int HW) {
+// Key blocks: one workgroup of KW waves per (key block, chunk of kv heads).
+// Wave w owns rows [w*R, (w+1)*R) of the block (R = B / KW) and keeps them in
+// registers, so the radius pass reuses them instead of reading the block again;
+// partial sums and maxima meet in LDS.  KW * R rows are in flight per
+// workgroup, enough to keep HBM busy with only nb workgroups.
+template <bool FP8, int D, int KW, int R>
+__global__ __launch_bounds__(64 * KW) void pool_k_kernel(
+    const void* __restrict__ k, const float* __restrict__ k_scale, float* __restrict__ kc,
+    float* __restrict__ kr, int64_t S, int Hkv, int B, int nb, int HW) {
   typedef RowLoad<FP8> L;
+  __shared__ f32x4 part[KW][64][2];
+  __shared__ float pmax[KW][64];
   const int j = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int gl = (tid * 8) / D, d = (tid * 8) % D;
+  const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int gl = (l * 8) / D, d = (l * 8) % D;
   const int g = blockIdx.y * HW + gl;
-  const bool active = g < Hkv;
+  const bool active = gl < HW && g < Hkv;
   const int64_t t0 = (int64_t)j * B;
   const int cnt = (int)((S - t0) < B ? (S - t0) : B);
   const size_t row_bytes = (size_t)Hkv * D * L::elem_bytes;
-  const unsigned char* base =
-      (const unsigned char*)k + (size_t)t0 * row_bytes + ((size_t)(active ? g : 0) * D + d) * L::elem_bytes;
+  const unsigned char* base = (const unsigned char*)k + (size_t)t0 * row_bytes +
+                              ((size_t)(active ? g : 0) * D + d) * L::elem_bytes;
+  const int r0 = w * R;
+  typename L::raw v[R];
+#pragma unroll
+  for (int u = 0; u < R; ++u)
+    if (active && r0 + u < cnt) v[u] = L::load(base + (size_t)(r0 + u) * row_bytes);
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (active) sum_rows<FP8>(base, row_bytes, cnt, acc);
+#pragma unroll
+  for (int u = 0; u < R; ++u)
+    if (active && r0 + u < cnt) L::add(acc, v[u]);
+  part[w][l][0] = f32x4{acc[0], acc[1], acc[2], acc[3]};
+  part[w][l][1] = f32x4{acc[4], acc[5], acc[6], acc[7]};
+  __syncthreads();
+  // every wave forms the same mean (fixed summation order over the waves)
+  float sum[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+  for (int ww = 0; ww < KW; ++ww) {
+    const f32x4 a0 = part[ww][l][0], a1 = part[ww][l][1];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sum[e] += a0[e];
+      sum[4 + e] += a1[e];
+    }
+  }
   const float scale = (FP8 && active) ? k_scale[(size_t)g * nb + j] : 1.0f;
   const float mul = scale / (float)cnt;
   float c[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) c[e] = acc[e] * mul;
-  if (active) {
+  for (int e = 0; e < 8; ++e) c[e] = sum[e] * mul;
+  if (w == 0 && active) {
     float* dst = kc + ((size_t)g * nb + j) * D + d;
     *(f32x4*)dst = f32x4{c[0], c[1], c[2], c[3]};
     *(f32x4*)(dst + 4) = f32x4{c[4], c[5], c[6], c[7]};
   }
-  if (!kr) return;
-  // second pass over the (now cache-resident) block: largest distance from the mean
+  if (!kr) return;  // uniform: no barrier follows for anyone
+  // largest distance of this wave's rows from the mean
   float mx = 0.f;
-  for (int t = 0; t < cnt; t += 4) {
-    typename L::raw v[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (active && t + u < cnt) v[u] = L::load(base + (size_t)(t + u) * row_bytes);
+  for (int u = 0; u < R; ++u) {
+    float pt = 0.f;
+    if (active && r0 + u < cnt) {
+      float x[8];
+      L::decode(x, v[u]);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      float part = 0.f;
-      if (active && t + u < cnt) {
-        float x[8];
-        L::decode(x, v[u]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float df = x[e] * scale - c[e];
-          part += df * df;
-        }
+      for (int e = 0; e < 8; ++e) {
+        const float df = x[e] * scale - c[e];
+        pt += df * df;
       }
-      part = head_lane_sum<D>(part);
-      if (t + u < cnt) mx = fmaxf(mx, part);
     }
+    pt = head_lane_sum<D>(pt);
+    mx = fmaxf(mx, pt);
   }
-  if (active && d == 0) kr[(size_t)g * nb + j] = sqrtf(mx);
+  pmax[w][l] = mx;
+  __syncthreads();
+  if (w == 0 && active && d == 0) {
+    float m = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < KW; ++ww) m = fmaxf(m, pmax[ww][l]);
+    kr[(size_t)g * nb + j] = sqrtf(m);
+  }
 }
 
 template <bool FP8, int D>
@@ -224,10 +254,15 @@ hipError_t launch_pool_t(const Shape& sh, const void* q, const void* k, const fl
                      sh.per_group, HW);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int HWK = sh.Hkv < maxh ? sh.Hkv : maxh;
+  // key blocks: 64 threads cover 512 / D heads; eight waves split the block's rows
+  const int HWK = 512 / D;
   dim3 gk(sh.nb, (sh.Hkv + HWK - 1) / HWK);
-  hipLaunchKernelGGL((pool_k_kernel<FP8, D>), gk, dim3(HWK * D / 8), 0, stream, k, k_scale,
-                     k_centroid, k_radius, sh.S, sh.Hkv, sh.B, sh.nb, HWK);
+  if (sh.B == 128)
+    hipLaunchKernelGGL((pool_k_kernel<FP8, D, 8, 16>), gk, dim3(512), 0, stream, k, k_scale,
+                       k_centroid, k_radius, sh.S, sh.Hkv, sh.B, sh.nb, HWK);
+  else
+    hipLaunchKernelGGL((pool_k_kernel<FP8, D, 8, 8>), gk, dim3(512), 0, stream, k, k_scale,
+                       k_centroid, k_radius, sh.S, sh.Hkv, sh.B, sh.nb, HWK);
   return hipGetLastError();
 }
 

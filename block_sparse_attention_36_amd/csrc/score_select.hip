@@ -3,8 +3,8 @@
 // Scores: s[u][i][j] = qbar[u][i] . kbar[kv(u)][j], j <= i, the mean-pooling inner
 // product ("Uncertainty-gated selection for block-sparse attention", technical
 // summary, Methodology step 1).  Computed on the fp32 matrix cores
-// (V_MFMA_F32_32X32X2_F32), one wave per 32x32 tile of the causal lower triangle,
-// so the scores keep full fp32 accuracy.
+// (V_MFMA_F32_32X32X2_F32), one workgroup per 64x64 tile of the causal lower
+// triangle, so the scores keep full fp32 accuracy.
 //
 // Selection (one wave per row (u, i)), on the candidates C_i = {0..i} minus the
 // forced blocks, ranked by descending score with the lowest index first on ties:
@@ -33,31 +33,48 @@ namespace {
 
 // ------------------------------------------------------------------ scores
 
-__global__ __launch_bounds__(64) void score_kernel(const float* __restrict__ qc,
-                                                   const float* __restrict__ kc,
-                                                   float* __restrict__ scores, int nb, int D,
-                                                   int G, int per_group) {
+// One workgroup of four waves per 64 x 64 tile of the causal lower triangle
+// (wave w: the 32 x 32 sub-tile (w / 2, w % 2)).  The tile's 64 query and 64 key
+// centroids are staged through LDS 32 dimensions at a time with coalesced
+// 16-byte loads; rows are padded to 33 floats so the per-lane operand reads of
+// one MFMA (32 rows, one column) hit distinct banks.
+__global__ __launch_bounds__(256) void score_kernel(const float* __restrict__ qc,
+                                                    const float* __restrict__ kc,
+                                                    float* __restrict__ scores, int nb, int D,
+                                                    int G, int per_group) {
   const int it = blockIdx.x, jt = blockIdx.y, u = blockIdx.z;
-  if (jt > it) return;
-  const int l = threadIdx.x;
-  const int hf = l >> 5;
+  if (jt > it) return;  // uniform for the workgroup
+  __shared__ float As[64 * 33], Bs[64 * 33];
+  const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
+  const int wi = w >> 1, wj = w & 1, hf = l >> 5;
   const int g = per_group ? u : u / G;
-  const int ia = it * 32 + (l & 31), jb = jt * 32 + (l & 31);
-  const float* arow = qc + ((size_t)u * nb + (ia < nb ? ia : nb - 1)) * D + hf * (D / 2);
-  const float* brow = kc + ((size_t)g * nb + (jb < nb ? jb : nb - 1)) * D + hf * (D / 2);
   f32x16 acc = {0};
-  // lane half hf contracts over d in [hf*D/2, (hf+1)*D/2): any split of the
-  // contraction index is valid as long as A and B use the same one
-  for (int k0 = 0; k0 < D / 2; k0 += 4) {
-    const f32x4 av = *(const f32x4*)(arow + k0);
-    const f32x4 bv = *(const f32x4*)(brow + k0);
+  for (int k0 = 0; k0 < D; k0 += 32) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[e], bv[e], acc, 0, 0, 0);
+    for (int t = 0; t < 2; ++t) {
+      const int idx = tid + 256 * t, row = idx >> 3, c4 = (idx & 7) * 4;
+      const int ia = min(it * 64 + row, nb - 1), jb = min(jt * 64 + row, nb - 1);
+      const f32x4 av = *(const f32x4*)(qc + ((size_t)u * nb + ia) * D + k0 + c4);
+      const f32x4 bv = *(const f32x4*)(kc + ((size_t)g * nb + jb) * D + k0 + c4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        As[row * 33 + c4 + e] = av[e];
+        Bs[row * 33 + c4 + e] = bv[e];
+      }
+    }
+    __syncthreads();
+    // A: row wi*32 + l%32, B: column wj*32 + l%32; lane half hf takes k = 2s + hf
+    const float* ar = As + (wi * 32 + (l & 31)) * 33 + hf;
+    const float* br = Bs + (wj * 32 + (l & 31)) * 33 + hf;
+#pragma unroll
+    for (int st = 0; st < 16; ++st)
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(ar[2 * st], br[2 * st], acc, 0, 0, 0);
+    __syncthreads();
   }
-  const int j = jt * 32 + (l & 31);
+  const int j = jt * 64 + wj * 32 + (l & 31);
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
-    const int i = it * 32 + (v >> 2) * 8 + hf * 4 + (v & 3);
+    const int i = it * 64 + wi * 32 + (v >> 2) * 8 + hf * 4 + (v & 3);
     if (i < nb && j <= i) scores[((size_t)u * nb + i) * nb + j] = acc[v];
   }
 }
@@ -537,29 +554,57 @@ __global__ __launch_bounds__(256) void select_reg_kernel(SelArgs a) {
 
 // row_ptr is clamped to the col_idx capacity, so a reader of the CSR can never
 // index past the buffer (the capacity bound makes the clamp a no-op).
+// Exclusive scan of the row counts in one workgroup: thread t owns a contiguous
+// chunk (a multiple of 4 rows, read and written as 16-byte vectors), the chunk
+// sums are scanned with wave shuffles and one LDS step across the 16 waves.
+// Offsets are clamped to the col_idx capacity.
 __global__ __launch_bounds__(1024) void scan_kernel(const int* __restrict__ counts,
                                                     int32_t* __restrict__ row_ptr, int rows,
                                                     int64_t capacity) {
-  __shared__ int part[1024];
-  const int t = threadIdx.x;
-  const int chunk = (rows + 1023) / 1024;
-  const int r0 = t * chunk, r1 = min(rows, r0 + chunk);
+  __shared__ int wsum[16];
+  const int t = threadIdx.x, l = t & 63, w = t >> 6;
+  const int chunk = (((rows + 1023) / 1024) + 3) & ~3;
+  const int r0 = min(rows, t * chunk), r1 = min(rows, r0 + chunk);
+  typedef __attribute__((ext_vector_type(4))) int i32x4;
   int sum = 0;
-  for (int r = r0; r < r1; ++r) sum += counts[r];
-  part[t] = sum;
+  for (int r = r0; r < r1; r += 4) {
+    if (r + 4 <= r1) {
+      const i32x4 v = *(const i32x4*)(counts + r);
+      sum += v[0] + v[1] + v[2] + v[3];
+    } else {
+      for (int q = r; q < r1; ++q) sum += counts[q];
+    }
+  }
+  int x = sum;  // inclusive scan within the wave
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(x, o);
+    if (l >= o) x += v;
+  }
+  if (l == 63) wsum[w] = x;
   __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {
-    const int v = t >= o ? part[t - o] : 0;
-    __syncthreads();
-    part[t] += v;
-    __syncthreads();
+  int before = 0;
+  for (int ww = 0; ww < w; ++ww) before += wsum[ww];
+  int64_t run = (int64_t)before + x - sum;  // exclusive prefix of this chunk
+  auto clampc = [&](int64_t v) { return (int32_t)(v < capacity ? v : capacity); };
+  for (int r = r0; r < r1; r += 4) {
+    if (r + 4 <= r1) {
+      const i32x4 v = *(const i32x4*)(counts + r);
+      i32x4 o;
+      o[0] = clampc(run);
+      o[1] = clampc(run + v[0]);
+      o[2] = clampc(run + v[0] + v[1]);
+      o[3] = clampc(run + v[0] + v[1] + v[2]);
+      *(i32x4*)(row_ptr + r) = o;
+      run += v[0] + v[1] + v[2] + v[3];
+    } else {
+      for (int q = r; q < r1; ++q) {
+        row_ptr[q] = clampc(run);
+        run += counts[q];
+      }
+    }
   }
-  int64_t run = part[t] - sum;  // exclusive prefix
-  for (int r = r0; r < r1; ++r) {
-    row_ptr[r] = (int32_t)(run < capacity ? run : capacity);
-    run += counts[r];
-  }
-  if (t == 1023) row_ptr[rows] = (int32_t)(part[1023] < capacity ? part[1023] : capacity);
+  if (t == 1023) row_ptr[rows] = clampc((int64_t)before + x);
 }
 
 __global__ __launch_bounds__(256) void compact_kernel(const unsigned long long* __restrict__ mask,
@@ -614,9 +659,9 @@ hipError_t launch_score_select(const Shape& sh, const SelectConfig& cfg, const f
   unsigned long long* mask = (unsigned long long*)(ws + w.mask_off);
   int* counts = (int*)(ws + w.counts_off);
   const int nb = sh.nb, U = sh.U(), rows = U * nb, nw = (nb + 63) / 64;
-  const int NT = (nb + 31) / 32;
+  const int NT = (nb + 63) / 64;
 
-  hipLaunchKernelGGL(score_kernel, dim3(NT, NT, U), dim3(64), 0, stream, q_centroid, k_centroid,
+  hipLaunchKernelGGL(score_kernel, dim3(NT, NT, U), dim3(256), 0, stream, q_centroid, k_centroid,
                      scores, nb, sh.D, sh.G(), sh.per_group);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
