@@ -66,9 +66,16 @@ __global__ __launch_bounds__(256) void score_kernel(const float* __restrict__ qc
     // A: row wi*32 + l%32, B: column wj*32 + l%32; lane half hf takes k = 2s + hf
     const float* ar = As + (wi * 32 + (l & 31)) * 33 + hf;
     const float* br = Bs + (wj * 32 + (l & 31)) * 33 + hf;
+    float av[16], bv[16];  // all operands of the chunk requested before the first product
+#pragma unroll
+    for (int st = 0; st < 16; ++st) {
+      av[st] = ar[2 * st];
+      bv[st] = br[2 * st];
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int st = 0; st < 16; ++st)
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(ar[2 * st], br[2 * st], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[st], bv[st], acc, 0, 0, 0);
     __syncthreads();
   }
   const int j = jt * 64 + wj * 32 + (l & 31);
@@ -467,12 +474,16 @@ __global__ __launch_bounds__(256) void select_reg_kernel(SelArgs a) {
     if (!done && __popcll(ballot64(taken != 0ull)) >= 0 && steps >= 16) {
       // many blocks needed: bisection on the mass of {key >= x} (fixed-tree sums)
       by_extraction = false;
+      float pe[SPL];  // each candidate's probability, computed once for all steps
+#pragma unroll
+      for (int e = 0; e < SPL; ++e)
+        pe[e] = (e < nsl && sr.cand(e)) ? exp2f((key_float(sr.k[e]) - s0) * a.tau_log2e) / zsum
+                                        : 0.f;
       auto mass_ge = [&](unsigned x) {
         float m = 0.f;
 #pragma unroll
         for (int e = 0; e < SPL; ++e)
-          if (e < nsl && sr.cand(e) && sr.k[e] >= x)
-            m += exp2f((key_float(sr.k[e]) - s0) * a.tau_log2e) / zsum;
+          if (e < nsl && sr.cand(e) && sr.k[e] >= x) m += pe[e];
         return wave_sum(m);
       };
       unsigned t = 0u;
