@@ -65,6 +65,38 @@ def pool_select_bytes(cfg, nnz: int) -> float:
     return float(b)
 
 
+def pool_bytes(cfg) -> float:
+    """Algorithmic HBM bytes of the pool stage alone: Q and K read once (plus E4M3
+    scales), centroids, norms and radii written once."""
+    S, Hq, Hkv, D, nb, U = (cfg.seq_len, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim,
+                            cfg.num_blocks, cfg.num_units)
+    es = 1 if cfg.dtype == "fp8" else 2
+    b = S * (Hq + Hkv) * D * es
+    if cfg.dtype == "fp8":
+        b += (Hq + Hkv) * nb * 4
+    b += (U * nb * D + Hkv * nb * D) * 4 + (U * nb + Hkv * nb) * 4
+    return float(b)
+
+
+def copy_bandwidth(torch, dev, nbytes: int = 1 << 30, reps: int = 5) -> float:
+    """GB/s (read + write bytes) of a plain device-to-device copy of nbytes: the
+    HBM rate this GPU reaches on a trivially coalesced stream."""
+    src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2.0 * nbytes / (ms * 1e-3) / 1e9
+
+
 def source_hash(*names) -> str:
     h = hashlib.sha256()
     for n in names:
@@ -293,7 +325,7 @@ def main(argv=None) -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if cfg.dtype == "bf16" else "fp8-e4m3 inputs, bf16 MFMA",
+        "dtype": "bf16" if cfg.dtype == "bf16" else "fp8-e4m3 (QK on fp8 MFMA, PV on bf16 MFMA)",
         "data": "synthetic (seeded generator, random structure; no model weights)",
         "config": {"workload": cfg.name, "seq_len": cfg.seq_len, "num_q_heads": cfg.num_q_heads,
                    "num_kv_heads": cfg.num_kv_heads, "head_dim": cfg.head_dim,
@@ -317,6 +349,14 @@ def main(argv=None) -> int:
                         "gbs": round(ps_bytes / (ps_ms * 1e-3) / 1e9, 1),
                         "frac_hbm": round(ps_bytes / (ps_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
     }
+    copy_gbs = copy_bandwidth(torch, dev)
+    pb = pool_bytes(cfg)
+    res["pool_select"]["copy_gbs"] = round(copy_gbs, 1)
+    res["pool_select"]["frac_copy"] = round(ps_bytes / (ps_ms * 1e-3) / 1e9 / copy_gbs, 4)
+    res["pool_select"]["pool_only"] = {
+        "gb": round(pb / 1e9, 4), "gbs": round(pb / (float(pool_ms.mean()) * 1e-3) / 1e9, 1),
+        "frac_hbm": round(pb / (float(pool_ms.mean()) * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "frac_copy": round(pb / (float(pool_ms.mean()) * 1e-3) / 1e9 / copy_gbs, 4)}
     if args.calibrate_copy:
         src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev).fill_(1.0)
         dst = torch.empty_like(src)

@@ -31,9 +31,12 @@
 // rows first) and maps the heads of one GQA group at one query block to the
 // same XCD, so their shared K/V blocks meet in the same L2.
 //
-// FP8 inputs (OCP E4M3): the raw codes are DMA'd, then expanded to bf16 in LDS
-// (exact); q_scale and k_scale fold into the per-block logit scale and v_scale
-// into the probabilities.
+// FP8 inputs (OCP E4M3): S^T = K Q^T runs on the gfx950 FP8 matrix cores
+// (V_MFMA_SCALE_F32_32X32X64_F8F6F4 with unit block scales: products of E4M3
+// codes are exact in fp32, so this is the bf16 result at twice the rate), with K
+// read raw from LDS and Q held raw in registers; V is expanded to bf16 in LDS
+// (exact) for O^T = V^T P^T.  q_scale and k_scale fold into the per-block logit
+// scale and v_scale into the probabilities.
 #include "common.h"
 #include "launch.h"
 
@@ -84,6 +87,14 @@ __device__ __forceinline__ int swz(int r) {
   const int k = (r >> 1) & 7;
   return ((k & 1) << 2) | (k >> 1);
 }
+// Raw E4M3 tiles (rows of D bytes, 16-byte chunks c): XOR applied to the chunk
+// index so that the 16 rows of one chunk column sit on 16 distinct 16-byte
+// slots of the 256-byte bank window (D = 128: two rows per window; D = 64: four).
+template <int D>
+__device__ __forceinline__ int swz8(int r) {
+  return D == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3);
+}
+
 template <int D>
 __device__ __forceinline__ int k_off(int r, int c) {
   return r * (D * 2) + ((c ^ swz<D>(r)) << 4);
@@ -149,8 +160,8 @@ struct Stage {
   // products while the texture-address queue drains
   static constexpr int NI = 2 * RAW_TILE / (1024 * C::NW);
   static constexpr int RAW_STAGE = 2 * RAW_TILE;
-  // raw stages [0, 2*RAW_STAGE); FP8 adds the bf16 compute stage after them
-  static constexpr int LDS_BYTES = FP8 ? 2 * RAW_STAGE + C::STAGE : 2 * C::STAGE;
+  // raw stages [0, 2*RAW_STAGE); FP8 adds the bf16 V tile after them
+  static constexpr int LDS_BYTES = FP8 ? 2 * RAW_STAGE + C::TILE : 2 * C::STAGE;
   static_assert(NI >= 1 && 2 * RAW_TILE % (1024 * C::NW) == 0,
                 "tile must split into 1 KiB DMAs per issuing wave");
 
@@ -168,7 +179,7 @@ struct Stage {
         col = (((p % C::ROWB) >> 4) ^ swz<D>(r)) << 4;
       } else {
         r = p / D;
-        col = p % D;
+        col = (((p % D) >> 4) ^ swz8<D>(r)) << 4;
       }
       off[n] = (unsigned)r * rs + (unsigned)col;
     }
@@ -206,25 +217,21 @@ struct Stage {
     }
   }
 
-  // FP8 only: expand the raw E4M3 tiles of `raw` into the swizzled bf16 stage.
-  static __device__ __forceinline__ void expand(const unsigned char* raw, unsigned char* kt,
-                                                unsigned char* vt, int tid) {
-    constexpr int NC8 = D / 16;             // 16-code chunks per row
-    constexpr int PER = B * NC8 / C::NT;    // chunks per thread per tile
+  // FP8 only: expand the raw E4M3 V tile into the swizzled bf16 V tile.
+  static __device__ __forceinline__ void expand_v(const unsigned char* raw, unsigned char* vt,
+                                                  int tid) {
+    constexpr int NC8 = D / 16;           // 16-code chunks per row
+    constexpr int PER = B * NC8 / C::NT;  // chunks per thread
     static_assert(PER >= 1 && B * NC8 % C::NT == 0, "expand split");
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int n = 0; n < PER; ++n) {
+      const int ci = tid + C::NT * n;
+      const int r = ci / NC8, c = ci % NC8;
+      const u32x4 w = *(const u32x4*)(raw + r * D + ((c ^ swz8<D>(r)) << 4));
 #pragma unroll
-      for (int n = 0; n < PER; ++n) {
-        const int ci = tid + C::NT * n;
-        const int r = ci / NC8, c = ci % NC8;
-        const u32x4 w = *(const u32x4*)(raw + t * RAW_TILE + ci * 16);
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const u32x2 x0 = e4m3x4_to_bf16x4(w[2 * hh]), x1 = e4m3x4_to_bf16x4(w[2 * hh + 1]);
-          const int off = t ? v_off<D>(r, 2 * c + hh) : k_off<D>(r, 2 * c + hh);
-          *(u32x4*)((t ? vt : kt) + off) = u32x4{x0[0], x0[1], x1[0], x1[1]};
-        }
+      for (int hh = 0; hh < 2; ++hh) {
+        const u32x2 x0 = e4m3x4_to_bf16x4(w[2 * hh]), x1 = e4m3x4_to_bf16x4(w[2 * hh + 1]);
+        *(u32x4*)(vt + v_off<D>(r, 2 * c + hh)) = u32x4{x0[0], x0[1], x1[0], x1[1]};
       }
     }
   }
@@ -319,24 +326,32 @@ __global__ __launch_bounds__(64 * 2 * (B / 32), 1) void attn_fwd_kernel(AttnArgs
     if (nblk > 1) jraw = cidx[1];
   }
 
-  // ---- Q fragments (B operand of S^T = K Q^T): query column = lane % 32,
-  // contraction index d = ds*16 + hf*8 + [0, 8)
-  bf16x8 qf[C::NDS];
+  // ---- Q fragments (B operand of S^T = K Q^T), query column = lane % 32.
+  // bf16: contraction index d = ds*16 + hf*8 + [0, 8) of step ds.  E4M3: byte b
+  // of product m is d = m*64 + hf*32 + b, the same assignment the K operand reads
+  // use (any common assignment of the contraction index to operand bytes gives
+  // the same product).
+  bf16x8 qf[FP8 ? 1 : C::NDS];
+  i32x8 qf8[FP8 ? D / 64 : 1];
   const float qsc = FP8 ? a.q_scale[(size_t)h * nb + i] : 1.0f;
   const int qi = qq * 32 + (l & 31);  // this lane's query inside the block
   {
     // rows past the ragged end load the last row instead (their outputs are not stored)
     int64_t t = (int64_t)i * B + qi;
     t = t < a.S ? t : a.S - 1;
+    if (!FP8) {
 #pragma unroll
-    for (int ds = 0; ds < C::NDS; ++ds) {
-      const size_t off = ((size_t)t * a.Hq + h) * D + ds * 16 + hf * 8;
-      if (!FP8) {
+      for (int ds = 0; ds < C::NDS; ++ds) {
+        const size_t off = ((size_t)t * a.Hq + h) * D + ds * 16 + hf * 8;
         qf[ds] = __builtin_bit_cast(bf16x8, *(const u32x4*)((const uint16_t*)a.q + off));
-      } else {
-        const u32x2 raw = *(const u32x2*)((const uint8_t*)a.q + off);
-        const u32x2 lo = e4m3x4_to_bf16x4(raw[0]), hi = e4m3x4_to_bf16x4(raw[1]);
-        qf[ds] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+      }
+    } else {
+#pragma unroll
+      for (int mm = 0; mm < D / 64; ++mm) {
+        const uint8_t* src = (const uint8_t*)a.q + ((size_t)t * a.Hq + h) * D + mm * 64 + hf * 32;
+        const u32x4 lo = *(const u32x4*)src, hi = *(const u32x4*)(src + 16);
+        qf8[mm] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                        (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
       }
     }
   }
@@ -367,13 +382,13 @@ __global__ __launch_bounds__(64 * 2 * (B / 32), 1) void attn_fwd_kernel(AttnArgs
     }
     jcur = jn;
     jraw = n + 2 < nblk ? cidx[n + 2] : -1;
-    unsigned char* kt = lds + (n & 1) * ST::RAW_STAGE;
-    if (FP8) {
-      kt = lds + 2 * ST::RAW_STAGE;
-      ST::expand(lds + (n & 1) * ST::RAW_STAGE, kt, kt + C::TILE, tid);
-      lds_barrier();
-    }
+    const unsigned char* kt = lds + (n & 1) * ST::RAW_STAGE;
     const unsigned char* vt = kt + C::TILE;
+    if (FP8) {
+      ST::expand_v(kt + ST::RAW_TILE, lds + 2 * ST::RAW_STAGE, tid);
+      lds_barrier();
+      vt = lds + 2 * ST::RAW_STAGE;
+    }
     if (j < 0) continue;
 
     // ---- S^T = K Q^T: A = K rows (keys), B = Q columns (queries).
@@ -386,21 +401,49 @@ __global__ __launch_bounds__(64 * 2 * (B / 32), 1) void attn_fwd_kernel(AttnArgs
     f32x16 s[C::NKT];
 #pragma unroll
     for (int kt2 = 0; kt2 < C::NKT; ++kt2) s[kt2] = f32x16{0};
-    const unsigned char* krow = kt + krow0;
-    bf16x8 kf[C::NDS][C::NKT];
+    if (!FP8) {
+      const unsigned char* krow = kt + krow0;
+      bf16x8 kf[C::NDS][C::NKT];
 #pragma unroll
-    for (int ds = 0; ds < C::NDS; ++ds) {
-      const unsigned char* ka = krow + (((2 * ds) ^ kx) << 4);
+      for (int ds = 0; ds < C::NDS; ++ds) {
+        const unsigned char* ka = krow + (((2 * ds) ^ kx) << 4);
 #pragma unroll
-      for (int kt2 = 0; kt2 < C::NKT; ++kt2)
-        kf[ds][kt2] = *(const bf16x8*)(ka + kt2 * 32 * C::ROWB);
+        for (int kt2 = 0; kt2 < C::NKT; ++kt2)
+          kf[ds][kt2] = *(const bf16x8*)(ka + kt2 * 32 * C::ROWB);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ds = 0; ds < C::NDS; ++ds)
+#pragma unroll
+        for (int kt2 = 0; kt2 < C::NKT; ++kt2)
+          s[kt2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ds][kt2], qf[ds], s[kt2], 0, 0, 0);
+    } else {
+      // raw E4M3 rows of D bytes: bytes [32*hf, 32*hf + 32) of 64-byte slice mm are
+      // chunks 4*mm + 2*hf and the next one (swizzled by the row's low bits, the
+      // same for every key tile)
+      const unsigned char* krow = kt + (kh * C::KW + (l & 31)) * D;
+      const int sw = swz8<D>(l & 31);
+      i32x8 kf8[D / 64][C::NKT];
+#pragma unroll
+      for (int mm = 0; mm < D / 64; ++mm) {
+        const int c0 = 4 * mm + 2 * hf;
+#pragma unroll
+        for (int kt2 = 0; kt2 < C::NKT; ++kt2) {
+          const unsigned char* rp = krow + kt2 * 32 * D;
+          const u32x4 lo = *(const u32x4*)(rp + ((c0 ^ sw) << 4));
+          const u32x4 hi = *(const u32x4*)(rp + (((c0 + 1) ^ sw) << 4));
+          kf8[mm][kt2] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                               (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int mm = 0; mm < D / 64; ++mm)
+#pragma unroll
+        for (int kt2 = 0; kt2 < C::NKT; ++kt2)  // formats E4M3 x E4M3, block scales 2^0
+          s[kt2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf8[mm][kt2], qf8[mm], s[kt2],
+                                                                   0, 0, 0, 127, 0, 127);
     }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int ds = 0; ds < C::NDS; ++ds)
-#pragma unroll
-      for (int kt2 = 0; kt2 < C::NKT; ++kt2)
-        s[kt2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ds][kt2], qf[ds], s[kt2], 0, 0, 0);
 
     // ---- online softmax (log2 domain); lane = one query, registers = keys.
     // The running reference max only moves when the block max exceeds it by
@@ -512,6 +555,9 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
   const int G = a.Hq / a.Hkv;
   const int rows8 = (a.Hkv * a.nb + 7) / 8;
   static_assert(ST::LDS_BYTES <= 160 * 1024, "LDS budget");
+  typedef Cfg<D, B> C;
+  static_assert(C::NQW * (C::NDT * 16 * 64 + 2 * 64) * 4 <= ST::LDS_BYTES,
+                "the key-half merge area must fit in the tile memory");
   static bool attr_set = false;
   if (!attr_set) {
     (void)hipFuncSetAttribute((const void*)attn_fwd_kernel<D, B, FP8>,

@@ -35,9 +35,14 @@ def _small(name):
 
 
 SMALL = [s for c in CONFIGS for s in _small(c.name)]
+# every supported (head_dim, block_size) pair in both input formats, ragged tails
+SHAPES = [scaled(config_by_name(base), 4096 + tail, num_q_heads=8, num_kv_heads=2,
+                 head_dim=d, block_size=b, name=f"{base}-D{d}-B{b}")
+          for base, tail in (("gqa32k", 37), ("msa1m", 70))
+          for d, b in ((64, 64), (64, 128), (128, 64), (128, 128))]
 
 
-@pytest.mark.parametrize("cfg", SMALL, ids=[c.name for c in SMALL])
+@pytest.mark.parametrize("cfg", SMALL + SHAPES, ids=[c.name for c in SMALL + SHAPES])
 def test_small_full_parity(cfg):
     _gpu_or_skip()
     import bsa_check as K

@@ -122,11 +122,12 @@ def scaled(cfg: WorkloadConfig, seq_len: int, num_q_heads: int | None = None,
     """
     hq = num_q_heads if num_q_heads is not None else cfg.num_q_heads
     hkv = num_kv_heads if num_kv_heads is not None else cfg.num_kv_heads
-    nb = -(-seq_len // cfg.block_size)
+    name = over.pop("name", f"{cfg.name}@{seq_len}")
+    nb = -(-seq_len // over.get("block_size", cfg.block_size))
     kw = dict(seq_len=seq_len, num_q_heads=hq, num_kv_heads=hkv)
     if cfg.num_needles:
         kw["num_needles"] = max(1, min(cfg.num_needles, nb // 4))
     if cfg.structure == "pairs":
         kw["pairs_per_kv_head"] = max(1, min(cfg.pairs_per_kv_head, nb // 8))
     kw.update(over)
-    return dataclasses.replace(cfg, name=f"{cfg.name}@{seq_len}", **kw)
+    return dataclasses.replace(cfg, name=name, **kw)
