@@ -549,6 +549,316 @@ __global__ __launch_bounds__(64 * 2 * (B / 32), 1) void attn_fwd_kernel(AttnArgs
   }
 }
 
+// ---------------------------------------------------------------------------
+// Whole-block kernel: four waves per (query head, query block) (two for B = 64),
+// wave w owning queries [32w, 32w + 32) against all B keys of every kept block,
+// so no merge of partial results is needed.  One K tile and one V tile in LDS
+// (64 KiB at D = B = 128), which lets two workgroups share a CU: the two waves on
+// each SIMD then belong to independent rows and run out of phase, and one
+// workgroup's row set-up and memory waits are covered by the other's products.
+// Within a block, K(n+1) streams in while O += V(n) P(n) runs and V(n+1) while
+// S(n+1) = K(n+1) Q^T and its softmax run:
+//   S(n), P(n) | wait V(n), barrier | request K(n+1) | O += V(n) P(n) |
+//   wait K(n+1), barrier | request V(n+1)
+template <int D, int B>
+struct WCfg {
+  static constexpr int NW = B / 32;    // waves = 32-query groups
+  static constexpr int NT = 64 * NW;
+  static constexpr int NKT = B / 32;   // 32-key tiles per block
+  static constexpr int NDS = D / 16;
+  static constexpr int NDT = D / 32;
+  static constexpr int ROWB = D * 2;
+  static constexpr int TILE = B * ROWB;
+};
+
+template <int D, int B, bool FP8>
+struct WTiles {
+  typedef WCfg<D, B> C;
+  static constexpr int RAW_TILE = FP8 ? B * D : C::TILE;
+  static constexpr int NI = RAW_TILE / (1024 * C::NW);  // DMA instructions per wave per tile
+  static constexpr int KBUF = 0, VBUF = RAW_TILE, XV = 2 * RAW_TILE;
+  static constexpr int LDS_BYTES = FP8 ? 2 * RAW_TILE + C::TILE : 2 * C::TILE;
+  static_assert(NI >= 1 && RAW_TILE % (1024 * C::NW) == 0, "tile must split into 1 KiB DMAs");
+
+  static __device__ __forceinline__ void plan(const AttnArgs& a, int wave, int l, unsigned* off) {
+    constexpr int ES = FP8 ? 1 : 2;
+    const unsigned rs = (unsigned)(a.Hkv * D * ES);
+#pragma unroll
+    for (int n = 0; n < NI; ++n) {
+      const int p = (wave * NI + n) * 1024 + 16 * l;
+      int r, col;
+      if (!FP8) {
+        r = p / C::ROWB;
+        col = (((p % C::ROWB) >> 4) ^ swz<D>(r)) << 4;
+      } else {
+        r = p / D;
+        col = (((p % D) >> 4) ^ swz8<D>(r)) << 4;
+      }
+      off[n] = (unsigned)r * rs + (unsigned)col;
+    }
+  }
+
+  // this wave's share of tile `src` (K or V) of key block j into `dst`; rows past
+  // the ragged end re-read the last row (their logits are masked)
+  static __device__ __forceinline__ void issue(const AttnArgs& a, const void* src, int g, int j,
+                                               unsigned char* dst, int wave, const unsigned* off) {
+    constexpr int ES = FP8 ? 1 : 2;
+    const unsigned char* base =
+        (const unsigned char*)src + ((size_t)j * B * a.Hkv + (size_t)g) * D * ES;
+    const int64_t left = a.S - (int64_t)j * B;
+    if (left >= B) {
+#pragma unroll
+      for (int n = 0; n < NI; ++n) dma16(base, off[n], lds_addr(dst + (wave * NI + n) * 1024));
+    } else {
+      const unsigned rs = (unsigned)(a.Hkv * D * ES);
+      const unsigned last = (unsigned)(left - 1) * rs;
+#pragma unroll
+      for (int n = 0; n < NI; ++n) {
+        const unsigned col = off[n] % rs, rowoff = off[n] - col;
+        dma16(base, (rowoff < last ? rowoff : last) + col, lds_addr(dst + (wave * NI + n) * 1024));
+      }
+    }
+  }
+
+  static __device__ __forceinline__ void expand_v(const unsigned char* raw, unsigned char* vt,
+                                                  int tid) {
+    constexpr int NC8 = D / 16;
+    constexpr int PER = B * NC8 / C::NT;
+    static_assert(PER >= 1 && B * NC8 % C::NT == 0, "expand split");
+#pragma unroll
+    for (int n = 0; n < PER; ++n) {
+      const int ci = tid + C::NT * n;
+      const int r = ci / NC8, c = ci % NC8;
+      const u32x4 w = *(const u32x4*)(raw + r * D + ((c ^ swz8<D>(r)) << 4));
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const u32x2 x0 = e4m3x4_to_bf16x4(w[2 * hh]), x1 = e4m3x4_to_bf16x4(w[2 * hh + 1]);
+        *(u32x4*)(vt + v_off<D>(r, 2 * c + hh)) = u32x4{x0[0], x0[1], x1[0], x1[1]};
+      }
+    }
+  }
+};
+
+template <int D, int B, bool FP8>
+__global__ __launch_bounds__(64 * (B / 32), 2) void attn_whole_kernel(AttnArgs a) {
+  typedef WCfg<D, B> C;
+  typedef WTiles<D, B, FP8> ST;
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  const int tid = threadIdx.x, l = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hf = l >> 5;
+
+  // work order as in attn_fwd_kernel: kv-head major, longest query block first,
+  // the heads of one group at one query block on one XCD
+  const int G = a.Hq / a.Hkv, nb = a.nb;
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, t8 = bid >> 3;
+  const int hh = t8 % G;
+  const int r = (t8 / G) * 8 + xcd;
+  if (r >= a.Hkv * nb) return;  // padding workgroup (uniform: no barrier reached)
+  const int g = r / nb, i = nb - 1 - r % nb;
+  const int h = g * G + hh;
+  const int unit = a.per_group ? g : h;
+  const int row = unit * nb + i;
+  const int e0 = a.row_ptr[row], e1 = a.row_ptr[row + 1];
+  const int nblk = e1 - e0;
+
+  // kept block ids (and E4M3 scales) 64 at a time, lane L holding entry base + L,
+  // read back with V_READLANE; -1 marks an entry outside the causal range, whose
+  // block is loaded (block 0) but fully masked
+  int cbase = 0, cid = -1;
+  float cks = 1.f, cvs = 1.f;
+  auto load_chunk = [&](int base) {
+    cbase = base;
+    const int n = base + l;
+    const int j = n < nblk ? a.col_idx[e0 + n] : -1;
+    cid = (j >= 0 && j <= i) ? j : -1;
+    if (FP8) {
+      const size_t o = (size_t)g * nb + (cid < 0 ? 0 : cid);
+      cks = a.k_scale[o];
+      cvs = a.v_scale[o];
+    }
+  };
+  auto id_at = [&](int n) { return __builtin_amdgcn_readlane(cid, n - cbase); };
+  auto blk = [](int j) { return j < 0 ? 0 : j; };
+  unsigned doff[ST::NI];
+  ST::plan(a, wave, l, doff);
+  if (nblk > 0) {
+    load_chunk(0);
+    const int j0 = blk(id_at(0));
+    ST::issue(a, a.k, g, j0, lds + ST::KBUF, wave, doff);
+    ST::issue(a, a.v, g, j0, lds + ST::VBUF, wave, doff);
+  }
+
+  // Q fragments, as in attn_fwd_kernel
+  bf16x8 qf[FP8 ? 1 : C::NDS];
+  i32x8 qf8[FP8 ? D / 64 : 1];
+  const float qsc = FP8 ? a.q_scale[(size_t)h * nb + i] : 1.0f;
+  const int qi = wave * 32 + (l & 31);
+  {
+    int64_t t = (int64_t)i * B + qi;
+    t = t < a.S ? t : a.S - 1;
+    if (!FP8) {
+#pragma unroll
+      for (int ds = 0; ds < C::NDS; ++ds) {
+        const size_t off = ((size_t)t * a.Hq + h) * D + ds * 16 + hf * 8;
+        qf[ds] = __builtin_bit_cast(bf16x8, *(const u32x4*)((const uint16_t*)a.q + off));
+      }
+    } else {
+#pragma unroll
+      for (int mm = 0; mm < D / 64; ++mm) {
+        const uint8_t* src = (const uint8_t*)a.q + ((size_t)t * a.Hq + h) * D + mm * 64 + hf * 32;
+        const u32x4 lo = *(const u32x4*)src, hi = *(const u32x4*)(src + 16);
+        qf8[mm] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                        (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      }
+    }
+  }
+
+  f32x16 o[C::NDT];
+  float m = -INFINITY, lsum = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < C::NDT; ++dt) o[dt] = f32x16{0};
+
+  const int kx = hf ^ swz<D>(l & 31);
+  const int rlo = 4 * hf + ((l & 15) >> 2);
+  const int cb0 = (((l >> 4) & 1) * 16 + 4 * (l & 3)) * 2;
+  const int kfirst = hf * 4;
+  const int vrow0 = rlo * C::ROWB + (cb0 & 15);
+
+  wait_vmem_all();
+  lds_barrier();
+  for (int n = 0; n < nblk; ++n) {
+    const int j = id_at(n);
+    const float ksc =
+        FP8 ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cks), n - cbase)) : 1.0f;
+    const float vsc =
+        FP8 ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cvs), n - cbase)) : 1.0f;
+    int jn = 0;
+    if (n + 1 < nblk) {
+      if (n + 1 - cbase >= 64) load_chunk(cbase + 64);
+      jn = blk(id_at(n + 1));
+    }
+
+    // ---- S^T = K(n) Q^T and the online softmax (K(n) is in LDS)
+    f32x16 s[C::NKT];
+#pragma unroll
+    for (int kt2 = 0; kt2 < C::NKT; ++kt2) s[kt2] = f32x16{0};
+    if (!FP8) {
+      const unsigned char* krow = lds + ST::KBUF + (l & 31) * C::ROWB;
+#pragma unroll
+      for (int ds = 0; ds < C::NDS; ++ds) {
+        const unsigned char* ka = krow + (((2 * ds) ^ kx) << 4);
+        bf16x8 kf[C::NKT];
+#pragma unroll
+        for (int kt2 = 0; kt2 < C::NKT; ++kt2) kf[kt2] = *(const bf16x8*)(ka + kt2 * 32 * C::ROWB);
+#pragma unroll
+        for (int kt2 = 0; kt2 < C::NKT; ++kt2)
+          s[kt2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kt2], qf[ds], s[kt2], 0, 0, 0);
+      }
+    } else {
+      const unsigned char* krow = lds + ST::KBUF + (l & 31) * D;
+      const int sw = swz8<D>(l & 31);
+#pragma unroll
+      for (int mm = 0; mm < D / 64; ++mm) {
+        const int c0 = 4 * mm + 2 * hf;
+        i32x8 kf8[C::NKT];
+#pragma unroll
+        for (int kt2 = 0; kt2 < C::NKT; ++kt2) {
+          const unsigned char* rp = krow + kt2 * 32 * D;
+          const u32x4 lo = *(const u32x4*)(rp + ((c0 ^ sw) << 4));
+          const u32x4 hi = *(const u32x4*)(rp + (((c0 + 1) ^ sw) << 4));
+          kf8[kt2] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                           (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        }
+#pragma unroll
+        for (int kt2 = 0; kt2 < C::NKT; ++kt2)
+          s[kt2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf8[kt2], qf8[mm], s[kt2], 0, 0,
+                                                                   0, 127, 0, 127);
+      }
+    }
+    const float sl = a.scale_log2 * qsc * ksc;
+    float mx = -INFINITY;
+    if (j < 0 || j == i || (int64_t)j * B + B > a.S) {
+      int lim = -1;
+      if (j >= 0) {
+        const int64_t left = a.S - (int64_t)j * B - 1 - kfirst;
+        lim = (int)(left < 4 * B ? left : 4 * B);
+        if (j == i) lim = min(lim, qi - kfirst);
+      }
+#pragma unroll
+      for (int kt2 = 0; kt2 < C::NKT; ++kt2)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int kw = kt2 * 32 + (v >> 2) * 8 + (v & 3);
+          const float x = kw > lim ? -INFINITY : s[kt2][v];
+          s[kt2][v] = x;
+          mx = fmaxf(mx, x);
+        }
+    } else {
+#pragma unroll
+      for (int kt2 = 0; kt2 < C::NKT; ++kt2)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kt2][v]);
+    }
+    mx = max_with_other_half(mx) * sl;
+    const bool bump = mx > m + 8.0f;
+    if (__ballot(bump)) {
+      const float alpha = bump ? __builtin_amdgcn_exp2f(m - mx) : 1.0f;
+      m = bump ? mx : m;
+      lsum *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[dt][v] *= alpha;
+    }
+    const float nref = m == -INFINITY ? 0.f : -m;
+    float psum = 0.f;
+    u32x4 pk[C::NKT][2];
+#pragma unroll
+    for (int kt2 = 0; kt2 < C::NKT; ++kt2) probs(s[kt2], nref, sl, vsc, psum, pk[kt2]);
+    lsum += psum;
+
+    // ---- V(n) has landed everywhere and K(n) is free: request K(n + 1)
+    wait_vmem_all();
+    lds_barrier();
+    if (n + 1 < nblk) ST::issue(a, a.k, g, jn, lds + ST::KBUF, wave, doff);
+    const unsigned char* vt = lds + ST::VBUF;
+    if (FP8) {
+      ST::expand_v(lds + ST::VBUF, lds + ST::XV, tid);
+      lds_barrier();
+      vt = lds + ST::XV;
+    }
+#pragma unroll
+    for (int kt2 = 0; kt2 < C::NKT; ++kt2) pv_tile<D, B>(vt + vrow0, pk[kt2], o, kt2, rlo, cb0);
+
+    // ---- K(n + 1) has landed everywhere and V(n) is free: request V(n + 1)
+    wait_vmem_all();
+    lds_barrier();
+    if (n + 1 < nblk) ST::issue(a, a.v, g, jn, lds + ST::VBUF, wave, doff);
+  }
+
+  // ---- output: this wave owns its 32 queries outright
+  lsum += other_half(lsum);
+  const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+  const int64_t t = (int64_t)i * B + qi;
+  if (t < a.S) {
+    uint16_t* orow = (uint16_t*)a.out + ((size_t)t * a.Hq + h) * D;
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+      for (int vg = 0; vg < 4; ++vg) {
+        const int d = dt * 32 + vg * 8 + hf * 4;
+        *(u32x2*)(orow + d) = u32x2{pack_bf16x2(o[dt][4 * vg] * inv, o[dt][4 * vg + 1] * inv),
+                                    pack_bf16x2(o[dt][4 * vg + 2] * inv, o[dt][4 * vg + 3] * inv)};
+      }
+    if (a.lse && hf == 0)
+      a.lse[(size_t)h * a.S + t] = lsum > 0.f ? (m + log2f(lsum)) * kLn2 : -INFINITY;
+  }
+}
+
+constexpr bool kWholeBlock = true;
+
 template <int D, int B, bool FP8>
 hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
   typedef Stage<D, B, FP8> ST;
@@ -559,6 +869,17 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
   static_assert(C::NQW * (C::NDT * 16 * 64 + 2 * 64) * 4 <= ST::LDS_BYTES,
                 "the key-half merge area must fit in the tile memory");
   static bool attr_set = false;
+  if (kWholeBlock) {
+    typedef WTiles<D, B, FP8> WT;
+    if (!attr_set) {
+      (void)hipFuncSetAttribute((const void*)attn_whole_kernel<D, B, FP8>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, WT::LDS_BYTES);
+      attr_set = true;
+    }
+    hipLaunchKernelGGL((attn_whole_kernel<D, B, FP8>), dim3(rows8 * 8 * G), dim3(WCfg<D, B>::NT),
+                       WT::LDS_BYTES, stream, a);
+    return hipGetLastError();
+  }
   if (!attr_set) {
     (void)hipFuncSetAttribute((const void*)attn_fwd_kernel<D, B, FP8>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, ST::LDS_BYTES);

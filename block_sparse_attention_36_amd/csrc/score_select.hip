@@ -132,10 +132,15 @@ __device__ void topk_threshold(const float* vals, int nslots, int i, int sink, i
     need = 0;
     return;
   }
+  // Bisection for the largest key t with at least k candidates >= t.  A probe x
+  // with exactly k candidates >= x already decides the kept set ({key >= x},
+  // the same k candidates the full bisection keeps), so the search stops there.
   unsigned t = 0u;
   for (int bit = 31; bit >= 0; --bit) {
     const unsigned x = t | (1u << bit);
-    if (count_ge(vals, nslots, i, sink, x) >= k) t = x;
+    const int c = count_ge(vals, nslots, i, sink, x);
+    if (c >= k) t = x;
+    if (c == k) break;
   }
   const int gt = (t == 0xFFFFFFFFu) ? 0 : count_ge(vals, nslots, i, sink, t + 1u);
   T = t;
@@ -355,10 +360,13 @@ __device__ void topk_reg(const RowKeys<SPL>& r, int nsl, int nc, int k, unsigned
     need = 0;
     return;
   }
+  // (early exit as in topk_threshold: exactly k candidates >= x decide the set)
   unsigned t = 0u;
   for (int bit = 31; bit >= 0; --bit) {
     const unsigned x = t | (1u << bit);
-    if (count_ge_reg(r, nsl, x) >= k) t = x;
+    const int c = count_ge_reg(r, nsl, x);
+    if (c >= k) t = x;
+    if (c == k) break;
   }
   need = k - (t == 0xFFFFFFFFu ? 0 : count_ge_reg(r, nsl, t + 1u));
   T = t;
