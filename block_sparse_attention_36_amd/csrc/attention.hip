@@ -6,30 +6,29 @@
 // "What is MSA and how does it work": the main branch attends over the
 // preselected blocks only).  Softmax is computed online, block by block.
 //
-// Work decomposition: one workgroup per (query head, query block), with two
-// waves per SIMD.  For B = 128 the workgroup has eight waves: wave w takes the
-// 32 queries of quarter (w % 4) and the 64 keys of half (w / 4) of every kept
-// block, keeps its own running max, sum and output, and the two key halves are
-// merged once, at the end.  The two waves that share a SIMD work on different key
-// halves, so one can run its softmax on the VALU while the other keeps the
-// matrix core busy.  The score tile is computed transposed, S^T = K Q^T, so that
-// each lane holds one query column: the per-query max and sum are lane-local
-// except for a single exchange between the two 32-lane halves
-// (V_PERMLANE32_SWAP).  The probabilities then feed the second product
+// Work decomposition: one workgroup per (query head, query block); wave w (four
+// waves at B = 128, two at B = 64) owns queries [32w, 32w + 32) against all B
+// keys of every kept block and keeps its own running max, sum and output, so no
+// partial results are merged.  The score tile is computed transposed,
+// S^T = K Q^T, so that each lane holds one query column: the per-query max and
+// sum are lane-local except for a single exchange between the two 32-lane
+// halves (V_PERMLANE32_SWAP).  The probabilities then feed the second product
 // O^T = V^T P^T straight from registers as the B operand, and the V^T operand is
 // read from the row-major V tile with the gfx950 transposing LDS load
 // (DS_READ_B64_TR_B16), so V is never transposed in memory.
 //
-// Memory: K and V tiles are double-buffered in LDS (2 x 64 KiB at D = B = 128)
-// and filled by direct global->LDS DMA.  Block n + 1 is requested right after
-// the barrier that opens block n, so it streams in while block n is computed and
-// no registers hold staged data; one barrier per block suffices.  The kept block
-// ids are read one block ahead.  LDS rows are
-// XOR-swizzled in 16-byte chunks so that both the 16-byte K reads (32 rows, one
-// column) and the transposing V reads (4 rows x 4 chunks per 32 lanes) are free
-// of bank conflicts.  The grid is ordered by descending query block (longest
-// rows first) and maps the heads of one GQA group at one query block to the
-// same XCD, so their shared K/V blocks meet in the same L2.
+// Memory and occupancy: a workgroup holds one K tile and one V tile in LDS
+// (64 KiB at D = B = 128), filled by direct global->LDS DMA, so two workgroups
+// share each CU: the two waves on a SIMD then belong to independent rows and run
+// out of phase (one's softmax on the VALU beside the other's products), and one
+// row's set-up and memory waits are covered by the other's products.  Within a
+// block, K(n+1) streams in while O += V(n) P(n) runs, and V(n+1) while S(n+1)
+// and its softmax run (two barriers per block).  LDS rows are XOR-swizzled in
+// 16-byte chunks so that both the 16-byte K reads (32 rows, one column) and the
+// transposing V reads (4 rows x 4 chunks per 32 lanes) are free of bank
+// conflicts.  The grid is ordered kv-head major, by descending query block
+// (longest rows first), and maps the heads of one GQA group at one query block
+// to the same XCD, so their shared K/V blocks meet in the same L2.
 //
 // FP8 inputs (OCP E4M3): S^T = K Q^T runs on the gfx950 FP8 matrix cores
 // (V_MFMA_SCALE_F32_32X32X64_F8F6F4 with unit block scales: products of E4M3
@@ -58,20 +57,6 @@ struct AttnArgs {
   int64_t S;
   int Hq, Hkv, nb, per_group;
   float scale_log2;
-};
-
-template <int D, int B>
-struct Cfg {
-  static constexpr int NQW = B / 32;    // 32-query groups = waves per key half
-  static constexpr int NW = 2 * NQW;    // waves per workgroup
-  static constexpr int NT = 64 * NW;    // threads per workgroup
-  static constexpr int KW = B / 2;      // keys per wave per block
-  static constexpr int NKT = KW / 32;   // 32-key tiles per wave
-  static constexpr int NDS = D / 16;    // contraction steps of S^T = K Q^T
-  static constexpr int NDT = D / 32;    // 32-row d tiles of O^T
-  static constexpr int ROWB = D * 2;    // bytes per bf16 LDS row
-  static constexpr int TILE = B * ROWB; // one bf16 K or V tile in LDS
-  static constexpr int STAGE = 2 * TILE;
 };
 
 // XOR applied to the 16-byte chunk index of LDS row r, shared by the K and V
@@ -151,90 +136,15 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <int D, int B, bool FP8>
-struct Stage {
-  typedef Cfg<D, B> C;
-  static constexpr int RAW_TILE = FP8 ? B * D : C::TILE;  // bytes of K (or V) per block
-  // DMA instructions per issuing wave per tile: only the waves of key half 0
-  // request tiles, so that the half-1 waves sharing their SIMDs start on the
-  // products while the texture-address queue drains
-  static constexpr int NI = 2 * RAW_TILE / (1024 * C::NW);
-  static constexpr int RAW_STAGE = 2 * RAW_TILE;
-  // raw stages [0, 2*RAW_STAGE); FP8 adds the bf16 V tile after them
-  static constexpr int LDS_BYTES = FP8 ? 2 * RAW_STAGE + C::TILE : 2 * C::STAGE;
-  static_assert(NI >= 1 && 2 * RAW_TILE % (1024 * C::NW) == 0,
-                "tile must split into 1 KiB DMAs per issuing wave");
-
-  // Per-lane byte offsets of the NI DMA instructions inside one tile (row r of the
-  // tile at r * rs, chunk swizzled for bf16), shared by K and V; computed once.
-  static __device__ __forceinline__ void plan(const AttnArgs& a, int wave, int l, unsigned* off) {
-    constexpr int ES = FP8 ? 1 : 2;
-    const unsigned rs = (unsigned)(a.Hkv * D * ES);
-#pragma unroll
-    for (int n = 0; n < NI; ++n) {
-      const int p = ((wave % C::NQW) * NI + n) * 1024 + 16 * l;
-      int r, col;  // tile row and byte column of this lane's 16 bytes
-      if (!FP8) {
-        r = p / C::ROWB;
-        col = (((p % C::ROWB) >> 4) ^ swz<D>(r)) << 4;
-      } else {
-        r = p / D;
-        col = (((p % D) >> 4) ^ swz8<D>(r)) << 4;
-      }
-      off[n] = (unsigned)r * rs + (unsigned)col;
-    }
-  }
-
-  // DMA key block j of kv head g into raw stage `dst` (K tile then V tile); a
-  // no-op for the waves of key half 1.  Rows past the ragged end re-read the
-  // last row (their logits are masked).
-  static __device__ __forceinline__ void issue(const AttnArgs& a, int g, int j, unsigned char* dst,
-                                               int wave, const unsigned* off) {
-    if (wave >= C::NQW) return;
-    constexpr int ES = FP8 ? 1 : 2;
-    const size_t blk = ((size_t)j * B * a.Hkv + (size_t)g) * D * ES;
-    const unsigned char* kb = (const unsigned char*)a.k + blk;
-    const unsigned char* vb = (const unsigned char*)a.v + blk;
-    const int64_t left = a.S - (int64_t)j * B;
-    if (left >= B) {
-#pragma unroll
-      for (int n = 0; n < NI; ++n) {
-        const int base = ((wave % C::NQW) * NI + n) * 1024;
-        dma16(kb, off[n], lds_addr(dst + base));
-        dma16(vb, off[n], lds_addr(dst + RAW_TILE + base));
-      }
-    } else {
-      const unsigned rs = (unsigned)(a.Hkv * D * ES);
-      const unsigned last = (unsigned)(left - 1) * rs;  // ragged block: clamp the row
-#pragma unroll
-      for (int n = 0; n < NI; ++n) {
-        const int base = ((wave % C::NQW) * NI + n) * 1024;
-        const unsigned col = off[n] % rs, rowoff = off[n] - col;
-        const unsigned o = (rowoff < last ? rowoff : last) + col;
-        dma16(kb, o, lds_addr(dst + base));
-        dma16(vb, o, lds_addr(dst + RAW_TILE + base));
-      }
-    }
-  }
-
-  // FP8 only: expand the raw E4M3 V tile into the swizzled bf16 V tile.
-  static __device__ __forceinline__ void expand_v(const unsigned char* raw, unsigned char* vt,
-                                                  int tid) {
-    constexpr int NC8 = D / 16;           // 16-code chunks per row
-    constexpr int PER = B * NC8 / C::NT;  // chunks per thread
-    static_assert(PER >= 1 && B * NC8 % C::NT == 0, "expand split");
-#pragma unroll
-    for (int n = 0; n < PER; ++n) {
-      const int ci = tid + C::NT * n;
-      const int r = ci / NC8, c = ci % NC8;
-      const u32x4 w = *(const u32x4*)(raw + r * D + ((c ^ swz8<D>(r)) << 4));
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const u32x2 x0 = e4m3x4_to_bf16x4(w[2 * hh]), x1 = e4m3x4_to_bf16x4(w[2 * hh + 1]);
-        *(u32x4*)(vt + v_off<D>(r, 2 * c + hh)) = u32x4{x0[0], x0[1], x1[0], x1[1]};
-      }
-    }
-  }
+template <int D, int B>
+struct WCfg {
+  static constexpr int NW = B / 32;    // waves = 32-query groups
+  static constexpr int NT = 64 * NW;
+  static constexpr int NKT = B / 32;   // 32-key tiles per block
+  static constexpr int NDS = D / 16;
+  static constexpr int NDT = D / 32;
+  static constexpr int ROWB = D * 2;
+  static constexpr int TILE = B * ROWB;
 };
 
 // exp2 of key tile kt2: p = 2^(s*sl - m), summed per query, scaled by vsc (E4M3
@@ -260,7 +170,7 @@ __device__ __forceinline__ void probs(const f32x16& s, float nref, float sl, flo
 template <int D, int B>
 __device__ __forceinline__ void pv_tile(const unsigned char* vrow, const u32x4 (&pk)[2],
                                         f32x16 (&o)[D / 32], int kt2, int rlo, int cb0) {
-  typedef Cfg<D, B> C;
+  typedef WCfg<D, B> C;
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb) {
     const int step = (kt2 * 32 + sb * 16) * C::ROWB;
@@ -277,299 +187,10 @@ __device__ __forceinline__ void pv_tile(const unsigned char* vrow, const u32x4 (
   }
 }
 
-template <int D, int B, bool FP8>
-__global__ __launch_bounds__(64 * 2 * (B / 32), 1) void attn_fwd_kernel(AttnArgs a) {
-  typedef Cfg<D, B> C;
-  typedef Stage<D, B, FP8> ST;
-  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-  const int tid = threadIdx.x, l = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int qq = wave % C::NQW, kh = wave / C::NQW, hf = l >> 5;
-
-  // ---- (head, query block) of this workgroup.  Rows are ordered kv-head major
-  // (the whole chip works through one kv head's K/V at a time, a working set
-  // that stays resident in the last-level cache), longest query block first
-  // within a kv head, and the heads of one group at one query block share an
-  // XCD (workgroup id mod 8) so their common K/V blocks meet in one L2.
-  const int G = a.Hq / a.Hkv, nb = a.nb;
-  const int bid = blockIdx.x;
-  const int xcd = bid & 7, t8 = bid >> 3;
-  const int hh = t8 % G;
-  const int r = (t8 / G) * 8 + xcd;
-  if (r >= a.Hkv * nb) return;  // padding workgroup (uniform: no barrier reached)
-  const int g = r / nb, i = nb - 1 - r % nb;
-  const int h = g * G + hh;
-  const int unit = a.per_group ? g : h;
-  const int row = unit * nb + i;
-  const int e0 = a.row_ptr[row], e1 = a.row_ptr[row + 1];
-  const int nblk = e1 - e0;
-  // -1 marks an entry outside the causal range, which is skipped
-  const int32_t* cidx = a.col_idx + e0;
-  auto valid = [&](int j) { return (j >= 0 && j <= i) ? j : -1; };
-  unsigned doff[ST::NI];
-  ST::plan(a, wave, l, doff);
-  // Per-block values are fetched one block ahead with ordinary vector loads
-  // issued right after the loop's vmcnt(0) wait: block n + 1's id is loaded
-  // during block n - 1 and its E4M3 scales during block n, and each is first
-  // used after the next such wait, so neither ever stalls the loop.  (Scalar
-  // loads would share lgkmcnt with the LDS reads and, returning out of order,
-  // force every LDS wait down to zero.)
-  int jcur = -1, jraw = -1;
-  float kscur = 1.0f, vscur = 1.0f;
-  if (nblk > 0) {
-    jcur = valid(__builtin_amdgcn_readfirstlane(cidx[0]));
-    ST::issue(a, g, jcur < 0 ? 0 : jcur, lds, wave, doff);
-    if (FP8) {
-      kscur = a.k_scale[(size_t)g * nb + (jcur < 0 ? 0 : jcur)];
-      vscur = a.v_scale[(size_t)g * nb + (jcur < 0 ? 0 : jcur)];
-    }
-    if (nblk > 1) jraw = cidx[1];
-  }
-
-  // ---- Q fragments (B operand of S^T = K Q^T), query column = lane % 32.
-  // bf16: contraction index d = ds*16 + hf*8 + [0, 8) of step ds.  E4M3: byte b
-  // of product m is d = m*64 + hf*32 + b, the same assignment the K operand reads
-  // use (any common assignment of the contraction index to operand bytes gives
-  // the same product).
-  bf16x8 qf[FP8 ? 1 : C::NDS];
-  i32x8 qf8[FP8 ? D / 64 : 1];
-  const float qsc = FP8 ? a.q_scale[(size_t)h * nb + i] : 1.0f;
-  const int qi = qq * 32 + (l & 31);  // this lane's query inside the block
-  {
-    // rows past the ragged end load the last row instead (their outputs are not stored)
-    int64_t t = (int64_t)i * B + qi;
-    t = t < a.S ? t : a.S - 1;
-    if (!FP8) {
-#pragma unroll
-      for (int ds = 0; ds < C::NDS; ++ds) {
-        const size_t off = ((size_t)t * a.Hq + h) * D + ds * 16 + hf * 8;
-        qf[ds] = __builtin_bit_cast(bf16x8, *(const u32x4*)((const uint16_t*)a.q + off));
-      }
-    } else {
-#pragma unroll
-      for (int mm = 0; mm < D / 64; ++mm) {
-        const uint8_t* src = (const uint8_t*)a.q + ((size_t)t * a.Hq + h) * D + mm * 64 + hf * 32;
-        const u32x4 lo = *(const u32x4*)src, hi = *(const u32x4*)(src + 16);
-        qf8[mm] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                        (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-      }
-    }
-  }
-
-  f32x16 o[C::NDT];
-  float m = -INFINITY, lsum = 0.f;
-#pragma unroll
-  for (int dt = 0; dt < C::NDT; ++dt) o[dt] = f32x16{0};
-
-  const int krow0 = (kh * C::KW + (l & 31)) * C::ROWB;
-  const int kx = hf ^ swz<D>(l & 31);
-  const int rlo = 4 * hf + ((l & 15) >> 2);                  // row within a 16-key step
-  const int cb0 = (((l >> 4) & 1) * 16 + 4 * (l & 3)) * 2;  // byte column in a d tile
-  const int kfirst = kh * C::KW + hf * 4;                    // first key row of this lane
-
-  for (int n = 0; n < nblk; ++n) {
-    const int j = jcur;
-    const float ksc = kscur, vsc = vscur;
-    wait_vmem_all();  // this wave's share of block n has landed
-    lds_barrier();    // ... and every other wave's; all are done with block n - 1
-    const int jn = valid(__builtin_amdgcn_readfirstlane(jraw));
-    if (n + 1 < nblk) {
-      ST::issue(a, g, jn < 0 ? 0 : jn, lds + ((n + 1) & 1) * ST::RAW_STAGE, wave, doff);
-      if (FP8) {
-        kscur = a.k_scale[(size_t)g * nb + (jn < 0 ? 0 : jn)];
-        vscur = a.v_scale[(size_t)g * nb + (jn < 0 ? 0 : jn)];
-      }
-    }
-    jcur = jn;
-    jraw = n + 2 < nblk ? cidx[n + 2] : -1;
-    const unsigned char* kt = lds + (n & 1) * ST::RAW_STAGE;
-    const unsigned char* vt = kt + C::TILE;
-    if (FP8) {
-      ST::expand_v(kt + ST::RAW_TILE, lds + 2 * ST::RAW_STAGE, tid);
-      lds_barrier();
-      vt = lds + 2 * ST::RAW_STAGE;
-    }
-    if (j < 0) continue;
-
-    // ---- S^T = K Q^T: A = K rows (keys), B = Q columns (queries).
-    // Row kh*KW + kt2*32 + (l&31) has the same swizzle for every kt2 (it depends
-    // on the row's low 4 bits only), so one lane address per contraction step
-    // serves every key tile, the tile offset folding into the instruction.  All
-    // K fragments are requested before the first product (the scheduling
-    // barrier keeps the compiler from sinking each read onto its MFMA), so the
-    // products consume them as they arrive instead of waiting on each read.
-    f32x16 s[C::NKT];
-#pragma unroll
-    for (int kt2 = 0; kt2 < C::NKT; ++kt2) s[kt2] = f32x16{0};
-    if (!FP8) {
-      const unsigned char* krow = kt + krow0;
-      bf16x8 kf[C::NDS][C::NKT];
-#pragma unroll
-      for (int ds = 0; ds < C::NDS; ++ds) {
-        const unsigned char* ka = krow + (((2 * ds) ^ kx) << 4);
-#pragma unroll
-        for (int kt2 = 0; kt2 < C::NKT; ++kt2)
-          kf[ds][kt2] = *(const bf16x8*)(ka + kt2 * 32 * C::ROWB);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int ds = 0; ds < C::NDS; ++ds)
-#pragma unroll
-        for (int kt2 = 0; kt2 < C::NKT; ++kt2)
-          s[kt2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ds][kt2], qf[ds], s[kt2], 0, 0, 0);
-    } else {
-      // raw E4M3 rows of D bytes: bytes [32*hf, 32*hf + 32) of 64-byte slice mm are
-      // chunks 4*mm + 2*hf and the next one (swizzled by the row's low bits, the
-      // same for every key tile)
-      const unsigned char* krow = kt + (kh * C::KW + (l & 31)) * D;
-      const int sw = swz8<D>(l & 31);
-      i32x8 kf8[D / 64][C::NKT];
-#pragma unroll
-      for (int mm = 0; mm < D / 64; ++mm) {
-        const int c0 = 4 * mm + 2 * hf;
-#pragma unroll
-        for (int kt2 = 0; kt2 < C::NKT; ++kt2) {
-          const unsigned char* rp = krow + kt2 * 32 * D;
-          const u32x4 lo = *(const u32x4*)(rp + ((c0 ^ sw) << 4));
-          const u32x4 hi = *(const u32x4*)(rp + (((c0 + 1) ^ sw) << 4));
-          kf8[mm][kt2] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                               (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int mm = 0; mm < D / 64; ++mm)
-#pragma unroll
-        for (int kt2 = 0; kt2 < C::NKT; ++kt2)  // formats E4M3 x E4M3, block scales 2^0
-          s[kt2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf8[mm][kt2], qf8[mm], s[kt2],
-                                                                   0, 0, 0, 127, 0, 127);
-    }
-
-    // ---- online softmax (log2 domain); lane = one query, registers = keys.
-    // The running reference max only moves when the block max exceeds it by
-    // more than 8 (a factor 256), so the output rescale is rare; every
-    // probability stays below 2^8 and the result is the same up to rounding.
-    const float sl = a.scale_log2 * (FP8 ? qsc * ksc : 1.0f);
-    float mx = -INFINITY;
-    // causal mask on the diagonal block and the ragged tail: key (kt2, v) of this
-    // lane sits at offset kw = kt2*32 + (v>>2)*8 + (v&3) from the lane's first
-    // key; it is masked when kw exceeds a per-lane limit (block-dependent, so the
-    // comparisons stay inside the loop and only run on those blocks)
-    if ((j == i) || ((int64_t)j * B + kh * C::KW + C::KW > a.S)) {
-      const int64_t left = a.S - (int64_t)j * B - 1 - kfirst;  // last valid kw
-      int lim = (int)(left < 4 * B ? left : 4 * B);
-      if (j == i) lim = min(lim, qi - kfirst);
-#pragma unroll
-      for (int kt2 = 0; kt2 < C::NKT; ++kt2)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int kw = kt2 * 32 + (v >> 2) * 8 + (v & 3);
-          const float x = kw > lim ? -INFINITY : s[kt2][v];
-          s[kt2][v] = x;
-          mx = fmaxf(mx, x);
-        }
-    } else {
-#pragma unroll
-      for (int kt2 = 0; kt2 < C::NKT; ++kt2)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kt2][v]);
-    }
-    // block max on the raw scores (sl > 0), then one FMA + exp2 per element
-    mx = max_with_other_half(mx) * sl;
-    const bool bump = mx > m + 8.0f;  // also true for the first finite block max
-    if (__ballot(bump)) {
-      // lanes that do not move keep alpha = 1 (their max may still be -inf)
-      const float alpha = bump ? __builtin_amdgcn_exp2f(m - mx) : 1.0f;  // 0 from -inf
-      m = bump ? mx : m;
-      lsum *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < C::NDT; ++dt)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) o[dt][v] *= alpha;
-    }
-    const float nref = m == -INFINITY ? 0.f : -m;
-
-    // ---- exp2 + bf16 packing per key tile, each followed by O^T += V^T P^T for
-    // that tile (the next tile's exp2 is independent of this tile's products)
-    float psum = 0.f;
-    const unsigned char* vrow = vt + (kh * C::KW + rlo) * C::ROWB + (cb0 & 15);
-#pragma unroll
-    for (int kt2 = 0; kt2 < C::NKT; ++kt2) {
-      u32x4 pk[2];
-      probs(s[kt2], nref, sl, vsc, psum, pk);
-      pv_tile<D, B>(vrow, pk, o, kt2, rlo, cb0);
-    }
-    lsum += psum;
-  }
-
-  // ---- merge the two key halves: lanes first (sum of the halves' partial sums),
-  // then waves kh = 1 hand their state to kh = 0 through LDS
-  lsum += other_half(lsum);
-  lds_barrier();  // every wave is done with the last stage before it is reused
-  // O moves in 16-byte pieces: piece (dt, vg) of lane l at ((dt*4 + vg)*64 + l)*16
-  float* xo = (float*)lds + (size_t)qq * (C::NDT * 16 * 64 + 2 * 64);
-  float* xm = xo + C::NDT * 16 * 64;
-  float* xl = xm + 64;
-  if (kh == 1) {
-#pragma unroll
-    for (int dt = 0; dt < C::NDT; ++dt)
-#pragma unroll
-      for (int vg = 0; vg < 4; ++vg)
-        *(f32x4*)(xo + ((dt * 4 + vg) * 64 + l) * 4) =
-            f32x4{o[dt][4 * vg], o[dt][4 * vg + 1], o[dt][4 * vg + 2], o[dt][4 * vg + 3]};
-    xm[l] = m;
-    xl[l] = lsum;
-  }
-  lds_barrier();
-  if (kh == 1) return;
-
-  uint16_t* out = (uint16_t*)a.out;
-  const float m1 = xm[l], l1 = xl[l];
-  const float mt = fmaxf(m, m1);
-  const float mref = mt == -INFINITY ? 0.f : mt;
-  const float a0 = exp2f(m - mref), a1 = exp2f(m1 - mref);
-  const float lt = lsum * a0 + l1 * a1;
-  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-  const int64_t t = (int64_t)i * B + qi;
-  if (t < a.S) {
-    uint16_t* orow = out + ((size_t)t * a.Hq + h) * D;
-#pragma unroll
-    for (int dt = 0; dt < C::NDT; ++dt)
-#pragma unroll
-      for (int vg = 0; vg < 4; ++vg) {
-        const f32x4 x1 = *(const f32x4*)(xo + ((dt * 4 + vg) * 64 + l) * 4);
-        float y[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) y[e] = (o[dt][vg * 4 + e] * a0 + x1[e] * a1) * inv;
-        const int d = dt * 32 + vg * 8 + hf * 4;
-        *(u32x2*)(orow + d) = u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
-      }
-    if (a.lse && hf == 0)
-      a.lse[(size_t)h * a.S + t] = lt > 0.f ? (mt + log2f(lt)) * kLn2 : -INFINITY;
-  }
-}
-
 // ---------------------------------------------------------------------------
-// Whole-block kernel: four waves per (query head, query block) (two for B = 64),
-// wave w owning queries [32w, 32w + 32) against all B keys of every kept block,
-// so no merge of partial results is needed.  One K tile and one V tile in LDS
-// (64 KiB at D = B = 128), which lets two workgroups share a CU: the two waves on
-// each SIMD then belong to independent rows and run out of phase, and one
-// workgroup's row set-up and memory waits are covered by the other's products.
-// Within a block, K(n+1) streams in while O += V(n) P(n) runs and V(n+1) while
-// S(n+1) = K(n+1) Q^T and its softmax run:
+// Tiles of one workgroup and the order of one block's work:
 //   S(n), P(n) | wait V(n), barrier | request K(n+1) | O += V(n) P(n) |
 //   wait K(n+1), barrier | request V(n+1)
-template <int D, int B>
-struct WCfg {
-  static constexpr int NW = B / 32;    // waves = 32-query groups
-  static constexpr int NT = 64 * NW;
-  static constexpr int NKT = B / 32;   // 32-key tiles per block
-  static constexpr int NDS = D / 16;
-  static constexpr int NDT = D / 32;
-  static constexpr int ROWB = D * 2;
-  static constexpr int TILE = B * ROWB;
-};
 
 template <int D, int B, bool FP8>
 struct WTiles {
@@ -648,8 +269,10 @@ __global__ __launch_bounds__(64 * (B / 32), 2) void attn_whole_kernel(AttnArgs a
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hf = l >> 5;
 
-  // work order as in attn_fwd_kernel: kv-head major, longest query block first,
-  // the heads of one group at one query block on one XCD
+  // work order: kv-head major (the whole chip works through one kv head's K/V at
+  // a time, a working set that stays resident in the last-level cache), longest
+  // query block first within a kv head, and the heads of one group at one query
+  // block on one XCD (workgroup id mod 8), so their common K/V blocks meet in one L2
   const int G = a.Hq / a.Hkv, nb = a.nb;
   const int bid = blockIdx.x;
   const int xcd = bid & 7, t8 = bid >> 3;
@@ -690,7 +313,11 @@ __global__ __launch_bounds__(64 * (B / 32), 2) void attn_whole_kernel(AttnArgs a
     ST::issue(a, a.v, g, j0, lds + ST::VBUF, wave, doff);
   }
 
-  // Q fragments, as in attn_fwd_kernel
+  // ---- Q fragments (B operand of S^T = K Q^T), query column = lane % 32.
+  // bf16: contraction index d = ds*16 + hf*8 + [0, 8) of step ds.  E4M3: byte b
+  // of product mm is d = mm*64 + hf*32 + b, the same assignment the K operand
+  // reads use (any common assignment of the contraction index to operand bytes
+  // gives the same product).
   bf16x8 qf[FP8 ? 1 : C::NDS];
   i32x8 qf8[FP8 ? D / 64 : 1];
   const float qsc = FP8 ? a.q_scale[(size_t)h * nb + i] : 1.0f;
@@ -745,16 +372,26 @@ __global__ __launch_bounds__(64 * (B / 32), 2) void attn_whole_kernel(AttnArgs a
 #pragma unroll
     for (int kt2 = 0; kt2 < C::NKT; ++kt2) s[kt2] = f32x16{0};
     if (!FP8) {
+      // the K fragments of step ds + 1 are requested before the products of step
+      // ds (the scheduling barriers keep that order), one step of latency hidden
       const unsigned char* krow = lds + ST::KBUF + (l & 31) * C::ROWB;
+      bf16x8 kf[2][C::NKT];
+#pragma unroll
+      for (int kt2 = 0; kt2 < C::NKT; ++kt2)
+        kf[0][kt2] = *(const bf16x8*)(krow + (kx << 4) + kt2 * 32 * C::ROWB);
 #pragma unroll
       for (int ds = 0; ds < C::NDS; ++ds) {
-        const unsigned char* ka = krow + (((2 * ds) ^ kx) << 4);
-        bf16x8 kf[C::NKT];
+        if (ds + 1 < C::NDS) {
+          const unsigned char* ka = krow + (((2 * (ds + 1)) ^ kx) << 4);
 #pragma unroll
-        for (int kt2 = 0; kt2 < C::NKT; ++kt2) kf[kt2] = *(const bf16x8*)(ka + kt2 * 32 * C::ROWB);
+          for (int kt2 = 0; kt2 < C::NKT; ++kt2)
+            kf[(ds + 1) & 1][kt2] = *(const bf16x8*)(ka + kt2 * 32 * C::ROWB);
+        }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int kt2 = 0; kt2 < C::NKT; ++kt2)
-          s[kt2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kt2], qf[ds], s[kt2], 0, 0, 0);
+          s[kt2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ds & 1][kt2], qf[ds], s[kt2], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
     } else {
       const unsigned char* krow = lds + ST::KBUF + (l & 31) * D;
@@ -857,37 +494,20 @@ __global__ __launch_bounds__(64 * (B / 32), 2) void attn_whole_kernel(AttnArgs a
   }
 }
 
-constexpr bool kWholeBlock = true;
-
 template <int D, int B, bool FP8>
 hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
-  typedef Stage<D, B, FP8> ST;
+  typedef WTiles<D, B, FP8> WT;
+  static_assert(WT::LDS_BYTES <= 80 * 1024, "two workgroups per CU must fit the 160 KiB LDS");
   const int G = a.Hq / a.Hkv;
   const int rows8 = (a.Hkv * a.nb + 7) / 8;
-  static_assert(ST::LDS_BYTES <= 160 * 1024, "LDS budget");
-  typedef Cfg<D, B> C;
-  static_assert(C::NQW * (C::NDT * 16 * 64 + 2 * 64) * 4 <= ST::LDS_BYTES,
-                "the key-half merge area must fit in the tile memory");
   static bool attr_set = false;
-  if (kWholeBlock) {
-    typedef WTiles<D, B, FP8> WT;
-    if (!attr_set) {
-      (void)hipFuncSetAttribute((const void*)attn_whole_kernel<D, B, FP8>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, WT::LDS_BYTES);
-      attr_set = true;
-    }
-    hipLaunchKernelGGL((attn_whole_kernel<D, B, FP8>), dim3(rows8 * 8 * G), dim3(WCfg<D, B>::NT),
-                       WT::LDS_BYTES, stream, a);
-    return hipGetLastError();
-  }
   if (!attr_set) {
-    (void)hipFuncSetAttribute((const void*)attn_fwd_kernel<D, B, FP8>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, ST::LDS_BYTES);
+    (void)hipFuncSetAttribute((const void*)attn_whole_kernel<D, B, FP8>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, WT::LDS_BYTES);
     attr_set = true;
   }
-  hipLaunchKernelGGL((attn_fwd_kernel<D, B, FP8>), dim3(rows8 * 8 * G), dim3(Cfg<D, B>::NT),
-                     ST::LDS_BYTES,
-                     stream, a);
+  hipLaunchKernelGGL((attn_whole_kernel<D, B, FP8>), dim3(rows8 * 8 * G), dim3(WCfg<D, B>::NT),
+                     WT::LDS_BYTES, stream, a);
   return hipGetLastError();
 }
 
