@@ -330,12 +330,25 @@ __device__ __forceinline__ float key_float(unsigned k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
+// One bit per register slot of a lane, in as many 64-bit words as SPL needs.
+template <int SPL>
+struct SlotBits {
+  static constexpr int NWD = (SPL + 63) / 64;
+  unsigned long long w[NWD];
+  __device__ __forceinline__ void clear() {
+#pragma unroll
+    for (int q = 0; q < NWD; ++q) w[q] = 0ull;
+  }
+  __device__ __forceinline__ bool get(int e) const { return (w[e >> 6] >> (e & 63)) & 1ull; }
+  __device__ __forceinline__ void set(int e) { w[e >> 6] |= 1ull << (e & 63); }
+};
+
 template <int SPL>
 struct RowKeys {
-  static_assert(SPL >= 1 && SPL <= 64, "one bit per slot in a 64-bit mask");
+  static_assert(SPL >= 1 && SPL <= 128, "register form: at most 128 slots per lane");
   unsigned k[SPL];
-  unsigned long long cand_bits;  // bit e: slot e of this lane is a candidate
-  __device__ __forceinline__ bool cand(int e) const { return (cand_bits >> e) & 1ull; }
+  SlotBits<SPL> cand_bits;  // bit e: slot e of this lane is a candidate
+  __device__ __forceinline__ bool cand(int e) const { return cand_bits.get(e); }
 };
 
 // number of candidates with key >= x (wave-uniform)
@@ -372,8 +385,11 @@ __device__ void topk_reg(const RowKeys<SPL>& r, int nsl, int nc, int k, unsigned
   T = t;
 }
 
-template <int SPL>
+// FULL = false compiles the top-k and gate branches only (the rescue keys and the
+// mass probabilities would not fit in registers at 128 slots).
+template <int SPL, bool FULL>
 __global__ __launch_bounds__(256) void select_reg_kernel(SelArgs a) {
+  const bool use_b = FULL && a.use_b, use_p = FULL && a.use_p;
   const int l = lane_id();
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= a.rows) return;  // no workgroup barriers below
@@ -384,10 +400,10 @@ __global__ __launch_bounds__(256) void select_reg_kernel(SelArgs a) {
   const int nc = i > 0 ? i - (sink ? 1 : 0) : 0;
   const int nsl = i / 64 + 1;
   const float* srow = a.scores + ((size_t)u * nb + i) * nb;
-  const float qnv = a.use_b ? a.qn[(size_t)u * nb + i] : 0.f;
+  const float qnv = use_b ? a.qn[(size_t)u * nb + i] : 0.f;
 
   RowKeys<SPL> sr, br;
-  sr.cand_bits = 0ull;
+  sr.cand_bits.clear();
 #pragma unroll
   for (int e = 0; e < SPL; ++e) {
     sr.k[e] = 0u;
@@ -396,12 +412,12 @@ __global__ __launch_bounds__(256) void select_reg_kernel(SelArgs a) {
     if (e < nsl && j <= i) {
       const float sv = srow[j];
       sr.k[e] = float_key(sv);
-      if (a.use_b) {
+      if (use_b) {
         const float bv = fmaf(qnv, a.kr[(size_t)g * nb + j], sv);
         br.k[e] = float_key(bv);
         if (a.bound_out) a.bound_out[((size_t)u * nb + i) * nb + j] = bv;
       }
-      if (is_cand(j, i, sink)) sr.cand_bits |= 1ull << e;
+      if (is_cand(j, i, sink)) sr.cand_bits.set(e);
     }
   }
   br.cand_bits = sr.cand_bits;
@@ -409,7 +425,7 @@ __global__ __launch_bounds__(256) void select_reg_kernel(SelArgs a) {
   // softmax statistics over the candidates (gate and mass)
   float s0 = -INFINITY, zsum = 0.f;
   unsigned kmax = 0u;
-  const bool need_soft = (a.gate && a.top_k > 0) || a.use_p;
+  const bool need_soft = (a.gate && a.top_k > 0) || use_p;
   if (need_soft && nc > 0) {
     unsigned km = 0u;
 #pragma unroll
@@ -448,11 +464,12 @@ __global__ __launch_bounds__(256) void select_reg_kernel(SelArgs a) {
   }
 
   // base branch: shortest prefix of the ranking whose mass reaches mu
-  unsigned long long taken = 0ull;  // extraction result (bits per slot of this lane)
+  SlotBits<SPL> taken;  // extraction result (bits per slot of this lane)
+  taken.clear();
   bool by_extraction = true;
   unsigned Tm = 0xFFFFFFFFu;
   int needm = 0;
-  if (a.use_p && nc > 0) {
+  if (use_p && nc > 0) {
     float cum = 0.f;
     int steps = 0;
     bool done = false;
@@ -461,7 +478,7 @@ __global__ __launch_bounds__(256) void select_reg_kernel(SelArgs a) {
       int bj = 0x7FFFFFFF;
 #pragma unroll
       for (int e = 0; e < SPL; ++e)
-        if (e < nsl && sr.cand(e) && !((taken >> e) & 1ull) && sr.k[e] > bk) {
+        if (e < nsl && sr.cand(e) && !taken.get(e) && sr.k[e] > bk) {
           bk = sr.k[e];
           bj = e * 64 + l;
         }
@@ -475,11 +492,11 @@ __global__ __launch_bounds__(256) void select_reg_kernel(SelArgs a) {
       }
       if (bj == 0x7FFFFFFF) break;  // every candidate taken
       cum += exp2f((key_float(bk) - s0) * a.tau_log2e) / zsum;
-      if ((bj & 63) == l) taken |= 1ull << (bj >> 6);
+      if ((bj & 63) == l) taken.set(bj >> 6);
       ++steps;
       done = cum >= a.mass_threshold;
     }
-    if (!done && __popcll(ballot64(taken != 0ull)) >= 0 && steps >= 16) {
+    if (!done && steps >= 16) {
       // many blocks needed: bisection on the mass of {key >= x} (fixed-tree sums)
       by_extraction = false;
       float pe[SPL];  // each candidate's probability, computed once for all steps
@@ -524,7 +541,7 @@ __global__ __launch_bounds__(256) void select_reg_kernel(SelArgs a) {
   // rescue branch: top ceil(phi*|C_i|) by the bound
   unsigned Tr = 0xFFFFFFFFu;
   int needr = 0;
-  if (a.use_b && nc > 0) {
+  if (use_b && nc > 0) {
     int nr = (int)ceil(a.rescue_fraction * (double)nc);
     nr = nr < nc ? nr : nc;
     topk_reg(br, nsl, nc, nr, Tr, needr);
@@ -545,16 +562,16 @@ __global__ __launch_bounds__(256) void select_reg_kernel(SelArgs a) {
       keep |= c && (sr.k[e] > Tk || ((tie >> l) & 1ull && runk + __popcll(tie & lt) < needk));
       runk += __popcll(tie);
     }
-    if (a.use_p) {
+    if (use_p) {
       if (by_extraction) {
-        keep |= (taken >> e) & 1ull;
+        keep |= taken.get(e);
       } else {
         const unsigned long long tie = ballot64(c && sr.k[e] == Tm);
         keep |= c && (sr.k[e] > Tm || ((tie >> l) & 1ull && runm + __popcll(tie & lt) < needm));
         runm += __popcll(tie);
       }
     }
-    if (a.use_b) {
+    if (use_b) {
       const unsigned long long tie = ballot64(c && br.k[e] == Tr);
       keep |= c && (br.k[e] > Tr || ((tie >> l) & 1ull && runr + __popcll(tie & lt) < needr));
       runr += __popcll(tie);
@@ -709,18 +726,21 @@ hipError_t launch_score_select(const Shape& sh, const SelectConfig& cfg, const f
   a.use_b = cfg.rescue_fraction > 0.0 ? 1 : 0;
   a.use_p = cfg.mass_threshold > 0.0f ? 1 : 0;
   a.per_wave_floats = nw * 64 * (1 + a.use_b + a.use_p);
-  // register form for rows up to 64*SPL = 4096 blocks, LDS form beyond
+  // register form for rows up to 64*SPL = 4096 blocks (8192 with the top-k and
+  // gate branches only), LDS form beyond
+  const bool topk_only = !a.use_b && !a.use_p;
   const int spl = nw <= 1 ? 1 : nw <= 2 ? 2 : nw <= 4 ? 4 : nw <= 8 ? 8 : nw <= 16 ? 16
-                  : nw <= 32 ? 32 : nw <= 64 ? 64 : 0;
+                  : nw <= 32 ? 32 : nw <= 64 ? 64 : (nw <= 128 && topk_only) ? 128 : 0;
   const dim3 rg((rows + 3) / 4), rb(256);
   switch (spl) {
-    case 1: hipLaunchKernelGGL(select_reg_kernel<1>, rg, rb, 0, stream, a); break;
-    case 2: hipLaunchKernelGGL(select_reg_kernel<2>, rg, rb, 0, stream, a); break;
-    case 4: hipLaunchKernelGGL(select_reg_kernel<4>, rg, rb, 0, stream, a); break;
-    case 8: hipLaunchKernelGGL(select_reg_kernel<8>, rg, rb, 0, stream, a); break;
-    case 16: hipLaunchKernelGGL(select_reg_kernel<16>, rg, rb, 0, stream, a); break;
-    case 32: hipLaunchKernelGGL(select_reg_kernel<32>, rg, rb, 0, stream, a); break;
-    case 64: hipLaunchKernelGGL(select_reg_kernel<64>, rg, rb, 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((select_reg_kernel<1, true>), rg, rb, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((select_reg_kernel<2, true>), rg, rb, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((select_reg_kernel<4, true>), rg, rb, 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((select_reg_kernel<8, true>), rg, rb, 0, stream, a); break;
+    case 16: hipLaunchKernelGGL((select_reg_kernel<16, true>), rg, rb, 0, stream, a); break;
+    case 32: hipLaunchKernelGGL((select_reg_kernel<32, true>), rg, rb, 0, stream, a); break;
+    case 64: hipLaunchKernelGGL((select_reg_kernel<64, true>), rg, rb, 0, stream, a); break;
+    case 128: hipLaunchKernelGGL((select_reg_kernel<128, false>), rg, rb, 0, stream, a); break;
     default: {
       const size_t per_wave_bytes = (size_t)a.per_wave_floats * sizeof(float);
       int waves = (int)(65536 / per_wave_bytes);
