@@ -193,15 +193,19 @@ def _pmc_rows(d: str, counter: str):
     return rows
 
 
+ATTN_KERNEL = "attn_whole_kernel"
+
+
 def summarize_pmc(fetch_dir: str, write_dir: str, out_json: str) -> int:
     """HBM bytes per attention launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
     each scaled by what the same counter reads for a plain copy of COPY_BYTES."""
     import statistics
-    out = {"kernel": "attn_fwd_kernel<128, 128, false>", "workload": "dual128k",
+    out = {"kernel": "attn_whole_kernel<128, 128, false>", "workload": "dual128k",
            "kernel_source_hash": source_hash("attention.hip", "common.h")}
+    others = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = _pmc_rows(d, counter)
-        att = [float(r["Counter_Value"]) * 1024 for r in rows if "attn_fwd_kernel" in r["Kernel_Name"]]
+        att = [float(r["Counter_Value"]) * 1024 for r in rows if ATTN_KERNEL in r["Kernel_Name"]]
         cp = [float(r["Counter_Value"]) * 1024 for r in rows
               if "copy" in r["Kernel_Name"].lower() and float(r["Counter_Value"]) * 1024 > COPY_BYTES / 2]
         if not att or not cp:
@@ -212,8 +216,19 @@ def summarize_pmc(fetch_dir: str, write_dir: str, out_json: str) -> int:
                                 "copy_raw_bytes": statistics.mean(cp), "copy_bytes": COPY_BYTES,
                                 "scale": factor,
                                 "bytes_per_launch": statistics.mean(att) / factor}
+        # the pool and selection kernels of the same run, per launch, calibrated alike
+        for r in rows:
+            name = r["Kernel_Name"]
+            short = next((k for k in ("pool_q_kernel", "pool_k_kernel", "score_kernel",
+                                      "select_reg_kernel", "select_kernel", "scan_kernel",
+                                      "compact_kernel") if k in name), None)
+            if short:
+                others.setdefault(short, {}).setdefault(counter.lower(), []).append(
+                    float(r["Counter_Value"]) * 1024 / factor)
     out["hbm_bytes_per_launch"] = (out["fetch_size"]["bytes_per_launch"] +
                                    out["write_size"]["bytes_per_launch"])
+    out["pool_select_kernels_bytes_per_launch"] = {
+        k: {c: round(statistics.mean(v)) for c, v in d.items()} for k, d in others.items()}
     with open(out_json, "w") as f:
         json.dump(out, f, indent=2)
     print(json.dumps(out))
@@ -335,7 +350,8 @@ def main(argv=None) -> int:
                        "rescue_fraction": cfg.rescue_fraction}},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic_from_profile(khash), "kernel": "attn_fwd_kernel<128,128>",
+                     "traffic": traffic_from_profile(khash),
+                     "kernel": f"{ATTN_KERNEL}<{cfg.head_dim},{cfg.block_size},{str(cfg.dtype == 'fp8').lower()}>",
                      "kernel_source_hash": khash},
         "stages_ms": {"pool": round(float(pool_ms.mean()), 4),
                       "score_select": round(float(sel_ms.mean()), 4),

@@ -98,7 +98,7 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const unsigned char* p) {
 // L landing at byte 16L; the swizzle is applied by choosing which global chunk
 // lane L fetches.  The loads are issued from inline asm (they have no register
 // results) so that the compiler does not serialise them against the LDS reads
-// of the other buffer; completion is awaited explicitly (s_waitcnt vmcnt) before
+// of the other tile; completion is awaited explicitly (S_WAITCNT vmcnt) before
 // the workgroup barrier.
 
 __device__ __forceinline__ unsigned lds_addr(const void* p) {
