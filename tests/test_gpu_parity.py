@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 import torch
 
-from workloads import CONFIGS, config_by_name, generate, scaled
+from workloads import CONFIGS, EXTRA_CONFIGS, config_by_name, generate, scaled
 
 pytestmark = pytest.mark.gpu
 
@@ -70,6 +70,26 @@ def test_full_size_sampled_parity(cfg):
           flush=True)
     del inp, run
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("cfg", EXTRA_CONFIGS, ids=[c.name for c in EXTRA_CONFIGS])
+def test_extra_workloads(cfg):
+    """Workloads beyond the five (the 128K dual-branch selection on E4M3 inputs):
+    a small scaled copy checked in full, then the full size on samples."""
+    _gpu_or_skip()
+    import bsa_check as K
+    small = scaled(cfg, 8192 + 100, num_q_heads=8, num_kv_heads=1)
+    for c, kw in ((small, {}), (cfg, dict(row_sample=48, unit_sample=24, score_sample=256))):
+        print(f"[parity-extra] {c.name} S={c.seq_len} {c.dtype}", flush=True)
+        inp = generate(c, "cuda")
+        run = K.run_gpu(c, inp)
+        rep = K.check_all(c, inp, run, **kw)
+        print(f"  rows={rep.rows_checked} ambiguous={rep.ambiguous_rows} fired={rep.gate_fired} "
+              f"max_abs={rep.max_abs:.3g} mean_abs={rep.mean_abs:.3g} lse={rep.lse_max:.3g}",
+              flush=True)
+        assert rep.ambiguous_rows <= max(1, rep.rows_checked // 100)
+        del inp, run
+        torch.cuda.empty_cache()
 
 
 MID = [scaled(config_by_name("msa1m"), 2000 * 128 + 17, num_q_heads=4, num_kv_heads=2),

@@ -8,5 +8,5 @@ a wide block hiding an outlier key) it is built from plain random draws and the
 mean query direction of the generated data.
 """
 
-from .configs import CONFIGS, WorkloadConfig, config_by_name, scaled  # noqa: F401
+from .configs import CONFIGS, EXTRA_CONFIGS, WorkloadConfig, config_by_name, scaled  # noqa: F401
 from .generate import Inputs, generate  # noqa: F401
