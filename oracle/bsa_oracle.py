@@ -18,6 +18,11 @@ The method, as the source pages describe it:
   * Uncertainty gate: when the best two candidates are nearly tied, the budget
     doubles from k to 2k (same page, lay summary "The Solution"; Methodology
     step 5 names the expansion factor rho = 2).
+  * Sigma gate (the page's own formulation): per (tile, head) the normalised
+    cut margin sigma = (s(k-1) - s(k)) / (s(0) - s(k)) of the sorted scores,
+    averaged over heads per tile; tiles whose mean falls in the lowest part of
+    the layer's empirical distribution expand to rho*k (same page, Methodology
+    steps 3-5).
   * RBS-Attention: a base branch keeps centroid-relevant blocks under its own
     threshold, a rescue branch flags blocks whose centroid may underestimate
     them using a per-(prompt, layer, head) key-block radius; the two masks are
@@ -50,7 +55,8 @@ import numpy as np
 __all__ = [
     "SelectParams", "decode_bf16", "decode_e4m3", "dequantize", "decode_inputs",
     "pool_queries", "pool_keys", "block_scores", "rescue_bounds", "candidate_sets",
-    "descending_order", "top_k", "gate_gap", "mass_prefix_length", "rescue_count",
+    "descending_order", "top_k", "gate_gap", "sigma_cut_margin", "sigma_gate_tiles",
+    "sigma_matrix", "tile_gate", "mass_prefix_length", "rescue_count",
     "select_row", "acceptable_row_sets", "select", "to_csr", "from_csr",
     "attend", "block_tokens", "attention_unit", "attention", "dense_causal_attention", "block_of", "unit_of_head",
     "kv_of_unit",
@@ -66,8 +72,10 @@ class SelectParams:
 
     top_k            k, the per-row budget beyond the forced blocks (0 = branch off)
     force_sink       also force block 0
-    gate             "none" or "top12_gap"
-    gate_threshold   theta: the gate fires when p(0) - p(1) < theta (float32)
+    gate             "none", "top12_gap" or "sigma_cut"
+    gate_threshold   top12_gap: theta, a row fires when p(0) - p(1) < theta;
+                     sigma_cut: q, a tile fires when its head-mean sigma lies in
+                     the lowest q fraction of the layer's tiles (float32)
     gate_factor      rho: the budget a fired row keeps is rho * k
     score_temperature tau in softmax(tau * s) (float32)
     mass_threshold   mu for the base branch (0 = branch off) (float32)
@@ -264,6 +272,68 @@ def gate_gap(s_row: np.ndarray, cands: list, tau: float) -> float:
     return float(p[0] - p[1])
 
 
+def sigma_cut_margin(s_row: np.ndarray, cands: list, k: int) -> float:
+    """Normalised cut margin of the top-k decision ("Uncertainty-gated selection
+    ...", technical summary, Methodology step 3):
+
+        sigma = (s(k-1) - s(k)) / (s(0) - s(k)),
+
+    with s(0) >= s(1) >= ... the candidates' raw scores sorted descending and
+    0-indexed, so s(k-1) is the last kept score and s(k) the first dropped one.
+    sigma near 1: the kept set stands well above the tail; near 0: the k-th and
+    (k+1)-th are (nearly) tied.  Only a row with a cut (|C| > k >= 1) has a
+    sigma (nan otherwise); when s(0) = s(k) every score down to the cut is tied
+    and sigma is 0.  With k = 1 the numerator equals the denominator, so sigma is
+    1 for every row without a tie at the top."""
+    if k < 1 or len(cands) <= k:
+        return math.nan
+    v = np.sort(np.asarray(s_row, dtype=np.float64)[cands])[::-1]
+    top, last_kept, first_dropped = v[0], v[k - 1], v[k]
+    if top == first_dropped:
+        return 0.0
+    return float((last_kept - first_dropped) / (top - first_dropped))
+
+
+def sigma_matrix(s: np.ndarray, k: int, force_sink: bool) -> np.ndarray:
+    """sigma[u, i] for every selection row (nan where tile i has no cut)."""
+    U, nb, _ = s.shape
+    sig = np.full((U, nb), np.nan)
+    for i in range(nb):
+        _, cands = candidate_sets(i, force_sink)
+        for u in range(U):
+            sig[u, i] = sigma_cut_margin(s[u, i], cands, k)
+    return sig
+
+
+def sigma_gate_tiles(sigma: np.ndarray, q: float):
+    """Per-tile decision of the sigma gate (same page, Methodology step 4).
+
+    sigma_bar[i] is the mean of sigma[:, i] over the selection units (each unit's
+    sigma stands for every head that shares its list, so this is the mean over
+    heads).  The layer's empirical distribution is that of sigma_bar over its
+    T tiles with a cut; tile i fires when the fraction of those tiles whose
+    sigma_bar is at most its own is at most q, i.e. when
+        #{t : sigma_bar[t] <= sigma_bar[i]} <= q * T   (q * T in IEEE double).
+    With distinct values that is the floor(q*T) most ambiguous tiles; a tile
+    without a cut never fires.  Returns (sigma_bar [nb], fired [nb] bool)."""
+    sbar = np.asarray(sigma, dtype=np.float64).mean(axis=0)
+    elig = ~np.isnan(sbar)
+    vals = sbar[elig]
+    limit = float(q) * float(len(vals))
+    fired = np.zeros(sbar.shape[0], dtype=bool)
+    for i in np.nonzero(elig)[0]:
+        fired[i] = np.count_nonzero(vals <= sbar[i]) <= limit
+    return sbar, fired
+
+
+def tile_gate(s: np.ndarray, p: "SelectParams"):
+    """(sigma_bar, fired) of every tile for the sigma gate, or None when the gate
+    is not the sigma gate or the top-k branch is off."""
+    if p.gate != "sigma_cut" or p.top_k <= 0:
+        return None
+    return sigma_gate_tiles(sigma_matrix(s, p.top_k, p.force_sink), p.gate_threshold)
+
+
 def mass_cumulative(s_row: np.ndarray, cands: list, tau: float):
     """(order, cum): candidates in descending order and the running sums of their
     softmax(tau * s) probabilities, cum[n] = mass of the first n (cum[0] = 0)."""
@@ -305,17 +375,22 @@ def _kept_set(i, s_row, b_row, p: SelectParams, gate_fired: bool, n_mass: int | 
     return sorted(kept)
 
 
-def select_row(i: int, s_row: np.ndarray, b_row: np.ndarray | None, p: SelectParams):
+def select_row(i: int, s_row: np.ndarray, b_row: np.ndarray | None, p: SelectParams,
+               tile_fired: bool = False):
     """Kept key blocks of one selection row, plus the gate decision.
 
     kept = forced  U  top-k (k doubled when the gate fires)  U  mass prefix  U  rescue,
     each branch present only when its parameter is on (RBS-Attention article,
-    third paragraph: independent thresholds per branch, masks fused).
+    third paragraph: independent thresholds per branch, masks fused).  The sigma
+    gate is decided per tile over the whole layer (``tile_gate``); its decision
+    for this row's tile comes in as ``tile_fired``.
     """
     _, cands = candidate_sets(i, p.force_sink)
     fired = False
     if p.gate == "top12_gap" and p.top_k > 0:
         fired = gate_gap(s_row, cands, p.score_temperature) < p.gate_threshold
+    elif p.gate == "sigma_cut" and p.top_k > 0:
+        fired = bool(tile_fired)
     n_mass = None
     if p.mass_threshold > 0.0:
         _, cum = mass_cumulative(s_row, cands, p.score_temperature)
@@ -323,13 +398,17 @@ def select_row(i: int, s_row: np.ndarray, b_row: np.ndarray | None, p: SelectPar
     return _kept_set(i, s_row, b_row, p, fired, n_mass), fired
 
 
-def acceptable_row_sets(i: int, s_row: np.ndarray, b_row, p: SelectParams, delta: float):
+def acceptable_row_sets(i: int, s_row: np.ndarray, b_row, p: SelectParams, delta: float,
+                        tile_fired_options=(False,)):
     """All kept sets reachable when a threshold decision whose float64 quantity lies
     within delta of its threshold is taken either way (a float32 evaluation of the
-    same softmax may land on the other side).  Returns (list of (kept, fired),
+    same softmax may land on the other side).  For the sigma gate the caller
+    passes the tile decisions it accepts.  Returns (list of (kept, fired),
     ambiguous flag)."""
     _, cands = candidate_sets(i, p.force_sink)
     gate_opts = [False]
+    if p.gate == "sigma_cut" and p.top_k > 0:
+        gate_opts = [bool(f) for f in tile_fired_options]
     if p.gate == "top12_gap" and p.top_k > 0:
         gap = gate_gap(s_row, cands, p.score_temperature)
         fired = gap < p.gate_threshold
@@ -360,9 +439,12 @@ def select(s: np.ndarray, b: np.ndarray | None, p: SelectParams):
     U, nb, _ = s.shape
     kept = [[None] * nb for _ in range(U)]
     fired = np.zeros((U, nb), dtype=bool)
+    tg = tile_gate(s, p)
+    tiles = tg[1] if tg is not None else np.zeros(nb, dtype=bool)
     for u in range(U):
         for i in range(nb):
-            kept[u][i], fired[u, i] = select_row(i, s[u, i], None if b is None else b[u, i], p)
+            kept[u][i], fired[u, i] = select_row(i, s[u, i], None if b is None else b[u, i], p,
+                                                 bool(tiles[i]))
     return kept, fired
 
 

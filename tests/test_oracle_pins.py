@@ -232,6 +232,163 @@ def test_gate_does_not_fire_on_clear_winner_and_gated_is_superset():
     assert not O.select_row(4, s, None, p)[1]
 
 
+# ---------------------------------------------------------------- sigma gate
+
+def test_sigma_hand_worked_rows():
+    # scores of five candidates, sorted 10, 7, 6, 2, 0
+    vals = np.array([6.0, 0.0, 10.0, 2.0, 7.0])
+    c = [0, 1, 2, 3, 4]
+    assert O.sigma_cut_margin(vals, c, 2) == pytest.approx((7 - 6) / (10 - 6), abs=1e-15)
+    assert O.sigma_cut_margin(vals, c, 3) == pytest.approx((6 - 2) / (10 - 2), abs=1e-15)
+    assert O.sigma_cut_margin(vals, c, 4) == pytest.approx((2 - 0) / (10 - 0), abs=1e-15)
+    # only the listed candidates count: dropping block 2 (the 10) changes the top
+    assert O.sigma_cut_margin(vals, [0, 1, 3, 4], 2) == pytest.approx((6 - 2) / (7 - 2), abs=1e-15)
+
+
+def test_sigma_arithmetic_progression_is_one_over_k():
+    # scores n, n-1, ..., 1 in shuffled positions: s(0) = n, s(k-1) = n-k+1 and
+    # s(k) = n-k, so sigma = 1/k; reading the cut one place off gives 1/(k+1)
+    rng = np.random.default_rng(40)
+    for n in (3, 5, 9, 17):
+        vals = rng.permutation(np.arange(1, n + 1)).astype(np.float64)
+        for k in range(1, n):
+            assert O.sigma_cut_margin(vals, list(range(n)), k) == pytest.approx(1.0 / k, abs=1e-15)
+
+
+def test_sigma_limits_and_no_cut():
+    c = [0, 1, 2, 3]
+    # tie between the last kept and the first dropped score: fully ambiguous
+    assert O.sigma_cut_margin(np.array([3.0, 9.0, 3.0, 1.0]), c, 2) == 0.0
+    # everything down to the cut tied: 0 by definition
+    assert O.sigma_cut_margin(np.array([4.0, 4.0, 4.0, 1.0]), c, 2) == 0.0
+    # kept set tied at the top and far above the rest: decisive
+    assert O.sigma_cut_margin(np.array([9.0, 1.0, 9.0, 0.0]), c, 2) == 1.0
+    # no cut when |C| <= k, and k = 0 has none either
+    assert math.isnan(O.sigma_cut_margin(np.arange(4.0), c, 4))
+    assert math.isnan(O.sigma_cut_margin(np.arange(4.0), c, 0))
+    rng = np.random.default_rng(41)
+    for _ in range(300):
+        n = int(rng.integers(2, 40))
+        vals = rng.normal(0, float(rng.uniform(0.01, 5)), size=n)
+        k = int(rng.integers(1, n))
+        sg = O.sigma_cut_margin(vals, list(range(n)), k)
+        assert 0.0 <= sg <= 1.0
+        # invariant under positive affine maps and under reordering of the candidates
+        a, b = float(rng.uniform(0.1, 10)), float(rng.normal(0, 10))
+        assert O.sigma_cut_margin(a * vals + b, list(range(n)), k) == pytest.approx(sg, abs=1e-9)
+        perm = rng.permutation(n)
+        assert O.sigma_cut_margin(vals[perm], list(range(n)), k) == pytest.approx(sg, abs=1e-15)
+
+
+def test_sigma_k1_degeneracy_and_the_lay_example():
+    # with k = 1 the kept score is the top one, so sigma is 1 unless s(0) = s(1)
+    rng = np.random.default_rng(42)
+    for _ in range(100):
+        n = int(rng.integers(2, 30))
+        vals = rng.normal(size=n)
+        assert O.sigma_cut_margin(vals, list(range(n)), 1) == 1.0
+    fx = json.load(open(os.path.join(GOLDEN, "gate_worked_example.json")))
+    s = np.array(fx["scores"] + [0.0])  # tile 2: candidates are blocks 0 and 1
+    assert O.sigma_cut_margin(s, [0, 1], 1) == 1.0
+    # a layer of such tiles: the gap gate fires on each, the sigma gate never does
+    nb = 6
+    srow = np.zeros((1, nb, nb))
+    for i in range(2, nb):
+        srow[0, i, i - 2:i] = fx["scores"]
+        srow[0, i, :i - 2] = -50.0
+    for q in (0.05, 0.5, 0.99):
+        p = O.SelectParams(top_k=1, gate="sigma_cut", gate_threshold=q)
+        sbar, fired = O.tile_gate(srow, p)
+        assert np.all(sbar[2:] == 1.0) and not fired.any()
+    pg = O.SelectParams(top_k=1, gate="top12_gap", gate_threshold=0.05)
+    assert all(O.select_row(i, srow[0, i], None, pg)[1] for i in range(2, nb))
+
+
+def test_sigma_tile_decision_hand_cases():
+    nan = math.nan
+    # one unit; tile 3 has no cut.  T = 4 tiles, q = 0.5: at most 2 may sit at or below
+    sbar, fired = O.sigma_gate_tiles(np.array([[0.5, 0.1, 0.3, nan, 0.2]]), 0.5)
+    assert list(fired) == [False, True, False, False, True]
+    # a tie across the boundary: three tiles share the lowest value, so with room for
+    # two none fires, with room for three all three do
+    sg = np.array([[0.2, 0.2, 0.2, 0.9]])
+    assert not O.sigma_gate_tiles(sg, 0.5)[1].any()
+    assert list(O.sigma_gate_tiles(sg, 0.75)[1]) == [True, True, True, False]
+    assert list(O.sigma_gate_tiles(sg, 1.0)[1]) == [True, True, True, True]
+    assert not O.sigma_gate_tiles(sg, 0.2)[1].any()
+    # the tile signal is the mean over units of each tile's column (3 units, 2 tiles)
+    sbar, _ = O.sigma_gate_tiles(np.array([[0.1, 0.9], [0.2, 0.6], [0.3, 0.3]]), 0.5)
+    assert sbar == pytest.approx([0.2, 0.6], abs=1e-15)
+
+
+def test_sigma_tile_decision_brute_force_by_sorting():
+    rng = np.random.default_rng(43)
+    for _ in range(100):
+        U, nb = int(rng.integers(1, 5)), int(rng.integers(1, 40))
+        sg = rng.uniform(0, 1, size=(U, nb))
+        sg[:, rng.random(nb) < 0.2] = math.nan
+        q = float(rng.uniform(0, 1))
+        sbar, fired = O.sigma_gate_tiles(sg, q)
+        elig = np.nonzero(~np.isnan(sbar))[0]
+        order = elig[np.argsort(sbar[elig], kind="stable")]
+        expect = set(order[: int(math.floor(q * len(elig)))].tolist())  # distinct values
+        assert set(np.nonzero(fired)[0].tolist()) == expect
+
+
+def test_sigma_gate_fires_on_planted_ambiguous_tiles():
+    # k = 2, sink forced: tile i has candidates 1..i-1, a cut from i = 4 on (8 tiles).
+    # Decisive tiles: two scores near 10 over a tail at 0 (sigma ~ 0.99); planted
+    # tiles: the 2nd and 3rd score nearly tied (sigma ~ 0.002).
+    nb, k, U = 12, 2, 2
+    s = np.full((U, nb, nb), -1.0)
+    planted = {5, 8, 11}
+    for u in range(U):
+        for i in range(nb):
+            s[u, i, 1:i] = 0.0
+            if i >= 4:
+                s[u, i, 1] = 10.0
+                if i in planted:
+                    s[u, i, 2], s[u, i, 3] = 5.0, 4.99
+                else:
+                    s[u, i, 2] = 9.9
+    p = O.SelectParams(top_k=k, force_sink=True, gate="sigma_cut", gate_threshold=3 / 8,
+                       gate_factor=2)
+    sbar, fired = O.tile_gate(s, p)
+    assert set(np.nonzero(fired)[0].tolist()) == planted
+    kept, flags = O.select(s, None, p)
+    for u in range(U):
+        for i in range(nb):
+            _, cands = O.candidate_sets(i, True)
+            forced = 2 if i > 0 else 1
+            assert flags[u, i] == (i in planted)
+            assert len(kept[u][i]) == min(len(cands), 2 * k if i in planted else k) + forced
+    # with room for two, the three planted tiles (equal sigma: the zero tail does
+    # not enter it) all stay off, since the percentile counts ties inclusively;
+    # once tile 11 is strictly the most ambiguous it fires alone
+    p2 = O.SelectParams(top_k=k, force_sink=True, gate="sigma_cut", gate_threshold=2 / 8)
+    assert not O.tile_gate(s, p2)[1].any()
+    s[:, 11, 3] = 4.999
+    assert set(np.nonzero(O.tile_gate(s, p2)[1])[0].tolist()) == {11}
+
+
+def test_sigma_gate_layer_superset_and_budget():
+    rng = np.random.default_rng(44)
+    U, nb, k = 3, 20, 3
+    s = rng.normal(0, 2, size=(U, nb, nb))
+    p = O.SelectParams(top_k=k, force_sink=True, gate="sigma_cut", gate_threshold=0.3,
+                       gate_factor=2).as_library_precision()
+    p0 = O.SelectParams(top_k=k, force_sink=True)
+    kept, flags = O.select(s, None, p)
+    kept0, _ = O.select(s, None, p0)
+    T = sum(1 for i in range(nb) if len(O.candidate_sets(i, True)[1]) > k)
+    fired_tiles = set(np.nonzero(flags[0])[0].tolist())
+    assert len(fired_tiles) == int(math.floor(p.gate_threshold * T))
+    for u in range(U):
+        assert set(np.nonzero(flags[u])[0].tolist()) == fired_tiles  # one decision per tile
+        for i in range(nb):
+            assert set(kept0[u][i]) <= set(kept[u][i])
+
+
 def test_mass_prefix_invariants():
     rng = np.random.default_rng(11)
     mu = float(np.float32(0.9))
