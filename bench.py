@@ -105,9 +105,9 @@ def source_hash(*names) -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(kernel_hash: str):
+def traffic_from_profile(kernel_hash: str, workload: str):
     """HBM bytes per attention launch from the committed counter summary, if it was
-    taken on the current kernel source; else None."""
+    taken on the current kernel source and on this workload; else None."""
     path = os.path.join(ROOT, "profiles", "attention_dual128k_counters.json")
     if not os.path.exists(path):
         return None
@@ -115,7 +115,7 @@ def traffic_from_profile(kernel_hash: str):
         rec = json.load(open(path))
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_hash") != kernel_hash:
+    if rec.get("kernel_source_hash") != kernel_hash or rec.get("workload") != workload:
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -276,7 +276,7 @@ def main(argv=None) -> int:
     gran = bsa.BSA_SEL_PER_GROUP if cfg.granularity == "group" else bsa.BSA_SEL_PER_QHEAD
     problem = bsa.make_problem(inp.q, inp.k, cfg.block_size, gran)
     params = bsa.make_params(cfg.top_k, cfg.force_sink,
-                             bsa.BSA_GATE_TOP12_GAP if cfg.gate == "top12_gap" else bsa.BSA_GATE_NONE,
+                             bsa.GATE_CODES[cfg.gate],
                              cfg.gate_threshold, cfg.gate_factor, cfg.score_temperature,
                              cfg.mass_threshold, cfg.rescue_fraction)
     rescue = cfg.rescue_fraction > 0
@@ -350,7 +350,7 @@ def main(argv=None) -> int:
                        "rescue_fraction": cfg.rescue_fraction}},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic_from_profile(khash),
+                     "traffic": traffic_from_profile(khash, cfg.name),
                      "kernel": f"{ATTN_KERNEL}<{cfg.head_dim},{cfg.block_size},{str(cfg.dtype == 'fp8').lower()}>",
                      "kernel_source_hash": khash},
         "stages_ms": {"pool": round(float(pool_ms.mean()), 4),

@@ -28,7 +28,8 @@ LIB_PATH = os.path.join(_HERE, "libbsa.so")
 BSA_OK = 0
 BSA_BF16, BSA_FP8_E4M3 = 0, 1
 BSA_SEL_PER_QHEAD, BSA_SEL_PER_GROUP = 0, 1
-BSA_GATE_NONE, BSA_GATE_TOP12_GAP = 0, 1
+BSA_GATE_NONE, BSA_GATE_TOP12_GAP, BSA_GATE_SIGMA_CUT = 0, 1, 2
+GATE_CODES = {"none": BSA_GATE_NONE, "top12_gap": BSA_GATE_TOP12_GAP, "sigma_cut": BSA_GATE_SIGMA_CUT}
 STATUS_NAMES = {0: "BSA_OK", 1: "BSA_ERR_INVALID_ARGUMENT", 2: "BSA_ERR_UNSUPPORTED",
                 3: "BSA_ERR_CAPACITY", 4: "BSA_ERR_WORKSPACE", 5: "BSA_ERR_DEVICE"}
 

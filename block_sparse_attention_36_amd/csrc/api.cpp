@@ -73,9 +73,9 @@ bsa_status check_params(const bsa_select_params* s) {
   if (s->top_k < 0) return fail(BSA_ERR_INVALID_ARGUMENT, "top_k %d < 0", s->top_k);
   if (s->force_sink != 0 && s->force_sink != 1)
     return fail(BSA_ERR_INVALID_ARGUMENT, "force_sink must be 0 or 1");
-  if (s->gate != BSA_GATE_NONE && s->gate != BSA_GATE_TOP12_GAP)
+  if (s->gate != BSA_GATE_NONE && s->gate != BSA_GATE_TOP12_GAP && s->gate != BSA_GATE_SIGMA_CUT)
     return fail(BSA_ERR_INVALID_ARGUMENT, "unknown gate %d", s->gate);
-  if (s->gate == BSA_GATE_TOP12_GAP) {
+  if (s->gate != BSA_GATE_NONE) {
     if (!(s->gate_threshold > 0.f && s->gate_threshold <= 1.f))
       return fail(BSA_ERR_INVALID_ARGUMENT, "gate_threshold must be in (0, 1]");
     if (s->gate_factor < 1) return fail(BSA_ERR_INVALID_ARGUMENT, "gate_factor must be >= 1");
@@ -95,7 +95,7 @@ bsa_status check_params(const bsa_select_params* s) {
 int64_t capacity_bound(const bsa::Shape& sh, const bsa_select_params* s) {
   int64_t per_unit = 0;
   const int64_t keff =
-      (int64_t)s->top_k * (s->gate == BSA_GATE_TOP12_GAP ? (int64_t)s->gate_factor : 1);
+      (int64_t)s->top_k * (s->gate != BSA_GATE_NONE ? (int64_t)s->gate_factor : 1);
   for (int64_t i = 0; i < sh.nb; ++i) {
     const int64_t nforced = (s->force_sink && i > 0) ? 2 : 1;
     const int64_t nc = i + 1 - nforced;
@@ -178,7 +178,8 @@ size_t bsa_score_select_workspace_size(const bsa_problem* problem, const bsa_sel
                                        int export_scores) {
   bsa::Shape sh;
   if (check_problem(problem, sh) != BSA_OK || check_params(params) != BSA_OK) return 0;
-  return bsa::select_workspace_layout(sh, export_scores != 0).total;
+  return bsa::select_workspace_layout(sh, export_scores != 0, params->gate == BSA_GATE_SIGMA_CUT)
+      .total;
 }
 
 bsa_status bsa_score_select(const bsa_problem* problem, const bsa_select_params* params,
@@ -206,13 +207,15 @@ bsa_status bsa_score_select(const bsa_problem* problem, const bsa_select_params*
   if (col_capacity < bound)
     return fail(BSA_ERR_CAPACITY, "col_capacity %lld < bound %lld", (long long)col_capacity,
                 (long long)bound);
-  const size_t need = bsa::select_workspace_layout(sh, scores_out != nullptr).total;
+  const size_t need =
+      bsa::select_workspace_layout(sh, scores_out != nullptr, params->gate == BSA_GATE_SIGMA_CUT)
+          .total;
   if (!workspace || workspace_bytes < need)
     return fail(BSA_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, need);
   bsa::SelectConfig cfg;
   cfg.top_k = params->top_k;
   cfg.force_sink = params->force_sink;
-  cfg.gate = params->gate == BSA_GATE_TOP12_GAP ? 1 : 0;
+  cfg.gate = params->gate == BSA_GATE_TOP12_GAP ? 1 : params->gate == BSA_GATE_SIGMA_CUT ? 2 : 0;
   cfg.gate_factor = params->gate_factor;
   cfg.gate_threshold = params->gate_threshold;
   cfg.temperature = params->score_temperature;

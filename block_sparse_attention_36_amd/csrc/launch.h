@@ -21,16 +21,18 @@ hipError_t launch_pool(const Shape& sh, const void* q, const void* k, const floa
                        float* k_radius, hipStream_t stream);
 
 struct SelectConfig {
-  int top_k, force_sink, gate, gate_factor;
+  int top_k, force_sink, gate, gate_factor;  // gate: 0 none, 1 top-1/top-2 gap, 2 sigma cut
   float gate_threshold, temperature, mass_threshold;
   double rescue_fraction;
 };
 
 // Workspace carve-up used by launch_score_select (byte offsets, 256-aligned).
 struct SelectWorkspace {
-  size_t scores_off, mask_off, counts_off, total;
+  size_t scores_off, mask_off, counts_off;
+  size_t sigma_off, mask_x_off, counts_x_off, keys_off, fire_off;  // sigma gate only
+  size_t total;
 };
-SelectWorkspace select_workspace_layout(const Shape& sh, bool export_scores);
+SelectWorkspace select_workspace_layout(const Shape& sh, bool export_scores, bool sigma_gate);
 
 hipError_t launch_score_select(const Shape& sh, const SelectConfig& cfg, const float* q_centroid,
                                const float* q_norm, const float* k_centroid,

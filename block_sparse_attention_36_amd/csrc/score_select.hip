@@ -17,6 +17,12 @@
 //   rescue : the first ceil(phi*|C_i|) ranked by b = s + ||qbar||*r (RBS-Attention,
 //            third and fourth paragraphs, the radius rescue branch);
 //   kept   : forced U top-k U base U rescue (the masks are unioned).
+// The sigma gate (same page, Methodology steps 3-5) decides per tile instead of
+// per row: each row records its cut margin sigma = (s(k-1) - s(k)) / (s(0) - s(k))
+// over its sorted candidate scores together with the extra blocks a budget of
+// rho*k would add; one workgroup then averages sigma over the units of every tile
+// and fires the tiles whose mean lies in the lowest q fraction of the layer's
+// tiles, and those tiles' rows take their extra blocks into the CSR.
 // Each branch is reduced to a threshold key T (the rank-k key, found by bisection
 // on the order-preserving integer image of the fp32 value) plus a count of
 // threshold ties admitted in index order.  All sums use a fixed reduction tree, so
@@ -101,10 +107,38 @@ struct SelArgs {
   float gate_threshold, tau_log2e, mass_threshold;
   double rescue_fraction;
   int use_b, use_p, per_wave_floats;
+  // sigma gate (gate == 2): per-row cut margin, the blocks that top-(rho*k) adds
+  // beyond the row's kept set, and their count
+  float* sigma;
+  unsigned long long* mask_x;
+  int* counts_x;
 };
 
 __device__ __forceinline__ bool is_cand(int j, int i, int sink) {
   return j < i && !(sink && j == 0);
+}
+
+// inverse of float_key
+__device__ __forceinline__ float key_float(unsigned k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+__device__ __forceinline__ unsigned wave_max_u(unsigned x) {
+  for (int o = 32; o >= 1; o >>= 1) x = max(x, (unsigned)__shfl_xor((int)x, o));
+  return x;
+}
+
+__device__ __forceinline__ unsigned wave_min_u(unsigned x) {
+  for (int o = 32; o >= 1; o >>= 1) x = min(x, (unsigned)__shfl_xor((int)x, o));
+  return x;
+}
+
+// Cut margin of a top-k decision from the keys of s(0) (best candidate), s(k-1)
+// (last kept) and s(k) (first dropped): (s(k-1) - s(k)) / (s(0) - s(k)), and 0
+// when s(0) = s(k) (every score down to the cut tied).
+__device__ __forceinline__ float cut_margin(unsigned k0, unsigned klast, unsigned kdrop) {
+  const float s0 = key_float(k0), a = key_float(klast), b = key_float(kdrop);
+  return s0 == b ? 0.f : (a - b) / (s0 - b);
 }
 
 // number of candidates whose key(vals[j]) >= X
@@ -191,7 +225,8 @@ __global__ __launch_bounds__(256) void select_kernel(SelArgs a) {
 
   // softmax statistics over the candidates (gate and mass)
   float s0 = -INFINITY, zsum = 0.f;
-  const bool need_soft = (a.gate && a.top_k > 0) || a.use_p;
+  const bool need_soft = (a.gate == 1 && a.top_k > 0) || a.use_p;
+  const bool sig = a.gate == 2 && a.top_k > 0;
   if (need_soft && nc > 0) {
     float mx = -INFINITY;
     for (int e = 0; e < nslots; ++e) {
@@ -223,7 +258,7 @@ __global__ __launch_bounds__(256) void select_kernel(SelArgs a) {
   int needk = 0;
   bool fired = false;
   if (a.top_k > 0) {
-    if (a.gate && nc >= 2) {
+    if (a.gate == 1 && nc >= 2) {
       // runner-up: best candidate other than the first (lowest-index) maximum
       int jmax = 0x7FFFFFFF;
       for (int e = 0; e < nslots; ++e) {
@@ -243,6 +278,10 @@ __global__ __launch_bounds__(256) void select_kernel(SelArgs a) {
     const int keff = a.top_k * (fired ? a.gate_factor : 1);
     topk_threshold(s, nslots, i, sink, nc, keff, Tk, needk);
   }
+  // sigma gate: the threshold of the expanded budget rho*k
+  unsigned Tx = 0xFFFFFFFFu;
+  int needx = 0;
+  if (sig) topk_threshold(s, nslots, i, sink, nc, a.top_k * a.gate_factor, Tx, needx);
 
   // base branch: shortest prefix of the order reaching mass mu
   unsigned Tm = 0xFFFFFFFFu;
@@ -282,19 +321,31 @@ __global__ __launch_bounds__(256) void select_kernel(SelArgs a) {
     topk_threshold(b, nslots, i, sink, nc, nr, Tr, needr);
   }
 
-  // union and mask emission
-  int runk = 0, runm = 0, runr = 0, count = 0;
+  // union and mask emission (with the sigma gate: the cut statistics of the
+  // top-k set and the expansion bits, blocks of top-(rho*k) not kept otherwise)
+  int runk = 0, runm = 0, runr = 0, runx = 0, count = 0, countx = 0;
+  unsigned ktop = 0u, kin = 0xFFFFFFFFu, kout = 0u;
   const unsigned long long lt = lanemask_lt();
   unsigned long long* mrow = a.mask + (size_t)row * a.nw;
   for (int e = 0; e < nslots; ++e) {
     const int j = e * 64 + l;
     const bool c = is_cand(j, i, sink);
     bool keep = (j == i) || (sink && j == 0 && j <= i);
+    bool inx = false;
     if (a.top_k > 0) {
       const unsigned key = c ? float_key(s[j]) : 0u;
       const unsigned long long tie = ballot64(c && key == Tk);
-      keep |= c && (key > Tk || ((tie >> l) & 1ull && runk + __popcll(tie & lt) < needk));
+      const bool ink = c && (key > Tk || ((tie >> l) & 1ull && runk + __popcll(tie & lt) < needk));
+      keep |= ink;
       runk += __popcll(tie);
+      if (sig) {
+        if (c) ktop = max(ktop, key);
+        if (ink) kin = min(kin, key);
+        else if (c) kout = max(kout, key);
+        const unsigned long long tx = ballot64(c && key == Tx);
+        inx = c && (key > Tx || ((tx >> l) & 1ull && runx + __popcll(tx & lt) < needx));
+        runx += __popcll(tx);
+      }
     }
     if (a.use_p) {
       const unsigned key = c ? float_key(s[j]) : 0u;
@@ -311,10 +362,25 @@ __global__ __launch_bounds__(256) void select_kernel(SelArgs a) {
     const unsigned long long word = ballot64(keep && j <= i);
     if (l == 0) mrow[e] = word;
     count += __popcll(word);
+    if (sig) {
+      const unsigned long long wx = ballot64(inx && !keep);
+      if (l == 0) a.mask_x[(size_t)row * a.nw + e] = wx;
+      countx += __popcll(wx);
+    }
+  }
+  if (sig) {
+    ktop = wave_max_u(ktop);
+    kin = wave_min_u(kin);
+    kout = wave_max_u(kout);
   }
   if (l == 0) {
     a.counts[row] = count;
-    if (a.gate_out) a.gate_out[row] = fired ? 1 : 0;
+    if (sig) {
+      a.counts_x[row] = countx;
+      a.sigma[row] = nc > a.top_k ? cut_margin(ktop, kin, kout) : 0.f;
+    } else if (a.gate_out) {
+      a.gate_out[row] = fired ? 1 : 0;
+    }
   }
 }
 
@@ -325,10 +391,6 @@ __global__ __launch_bounds__(256) void select_kernel(SelArgs a) {
 // cross-lane reduction; the base branch extracts maxima one at a time in the
 // ranking order (the usual case needs a handful) and falls back to bisection
 // on fixed-tree mass sums when more than 16 blocks are needed.
-
-__device__ __forceinline__ float key_float(unsigned k) {
-  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
-}
 
 // One bit per register slot of a lane, in as many 64-bit words as SPL needs.
 template <int SPL>
@@ -386,8 +448,9 @@ __device__ void topk_reg(const RowKeys<SPL>& r, int nsl, int nc, int k, unsigned
 }
 
 // FULL = false compiles the top-k and gate branches only (the rescue keys and the
-// mass probabilities would not fit in registers at 128 slots).
-template <int SPL, bool FULL>
+// mass probabilities would not fit in registers at 128 slots).  SIG compiles the
+// sigma gate's per-row part (its extra state stays out of the other forms).
+template <int SPL, bool FULL, bool SIG>
 __global__ __launch_bounds__(256) void select_reg_kernel(SelArgs a) {
   const bool use_b = FULL && a.use_b, use_p = FULL && a.use_p;
   const int l = lane_id();
@@ -425,7 +488,8 @@ __global__ __launch_bounds__(256) void select_reg_kernel(SelArgs a) {
   // softmax statistics over the candidates (gate and mass)
   float s0 = -INFINITY, zsum = 0.f;
   unsigned kmax = 0u;
-  const bool need_soft = (a.gate && a.top_k > 0) || use_p;
+  const bool need_soft = (a.gate == 1 && a.top_k > 0) || use_p;
+  const bool sig = SIG && a.gate == 2 && a.top_k > 0;
   if (need_soft && nc > 0) {
     unsigned km = 0u;
 #pragma unroll
@@ -446,7 +510,7 @@ __global__ __launch_bounds__(256) void select_reg_kernel(SelArgs a) {
   int needk = 0;
   bool fired = false;
   if (a.top_k > 0) {
-    if (a.gate && nc >= 2) {
+    if (a.gate == 1 && nc >= 2) {
       int jm = 0x7FFFFFFF;
 #pragma unroll
       for (int e = SPL - 1; e >= 0; --e)
@@ -462,6 +526,10 @@ __global__ __launch_bounds__(256) void select_reg_kernel(SelArgs a) {
     }
     topk_reg(sr, nsl, nc, a.top_k * (fired ? a.gate_factor : 1), Tk, needk);
   }
+  // sigma gate: the threshold of the expanded budget rho*k
+  unsigned Tx = 0xFFFFFFFFu;
+  int needx = 0;
+  if (sig) topk_reg(sr, nsl, nc, a.top_k * a.gate_factor, Tx, needx);
 
   // base branch: shortest prefix of the ranking whose mass reaches mu
   SlotBits<SPL> taken;  // extraction result (bits per slot of this lane)
@@ -547,8 +615,10 @@ __global__ __launch_bounds__(256) void select_reg_kernel(SelArgs a) {
     topk_reg(br, nsl, nc, nr, Tr, needr);
   }
 
-  // union and mask emission
-  int runk = 0, runm = 0, runr = 0, count = 0;
+  // union and mask emission (with the sigma gate: the cut statistics of the
+  // top-k set and the expansion bits, blocks of top-(rho*k) not kept otherwise)
+  int runk = 0, runm = 0, runr = 0, runx = 0, count = 0, countx = 0;
+  unsigned ktop = 0u, kin = 0xFFFFFFFFu, kout = 0u;
   const unsigned long long lt = lanemask_lt();
   unsigned long long* mrow = a.mask + (size_t)row * a.nw;
 #pragma unroll
@@ -557,10 +627,21 @@ __global__ __launch_bounds__(256) void select_reg_kernel(SelArgs a) {
     const int j = e * 64 + l;
     const bool c = sr.cand(e);
     bool keep = (j == i) || (sink && j == 0 && j <= i);
+    bool inx = false;
     if (a.top_k > 0) {
       const unsigned long long tie = ballot64(c && sr.k[e] == Tk);
-      keep |= c && (sr.k[e] > Tk || ((tie >> l) & 1ull && runk + __popcll(tie & lt) < needk));
+      const bool ink =
+          c && (sr.k[e] > Tk || ((tie >> l) & 1ull && runk + __popcll(tie & lt) < needk));
+      keep |= ink;
       runk += __popcll(tie);
+      if (sig) {
+        if (c) ktop = max(ktop, sr.k[e]);
+        if (ink) kin = min(kin, sr.k[e]);
+        else if (c) kout = max(kout, sr.k[e]);
+        const unsigned long long tx = ballot64(c && sr.k[e] == Tx);
+        inx = c && (sr.k[e] > Tx || ((tx >> l) & 1ull && runx + __popcll(tx & lt) < needx));
+        runx += __popcll(tx);
+      }
     }
     if (use_p) {
       if (by_extraction) {
@@ -579,10 +660,87 @@ __global__ __launch_bounds__(256) void select_reg_kernel(SelArgs a) {
     const unsigned long long word = ballot64(keep && j <= i);
     if (l == 0) mrow[e] = word;
     count += __popcll(word);
+    if (sig) {
+      const unsigned long long wx = ballot64(inx && !keep);
+      if (l == 0) a.mask_x[(size_t)row * a.nw + e] = wx;
+      countx += __popcll(wx);
+    }
+  }
+  if (sig) {
+    ktop = wave_max_u(ktop);
+    kin = wave_min_u(kin);
+    kout = wave_max_u(kout);
   }
   if (l == 0) {
     a.counts[row] = count;
-    if (a.gate_out) a.gate_out[row] = fired ? 1 : 0;
+    if (sig) {
+      a.counts_x[row] = countx;
+      a.sigma[row] = nc > a.top_k ? cut_margin(ktop, kin, kout) : 0.f;
+    } else if (a.gate_out) {
+      a.gate_out[row] = fired ? 1 : 0;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ sigma gate, per tile
+// One workgroup for the layer.  Tile i has a cut when |C_i| > k; its signal is
+// the mean of sigma over the U units (summed in unit order).  With T tiles that
+// have a cut and r = floor(q*T) (in double), tile i fires when at most r of
+// them have a mean <= its own, i.e. when its mean lies strictly below the
+// (r+1)-th smallest, found by bisection on the order-preserving keys.  Every
+// row of a fired tile then counts its expansion blocks, and the per-tile
+// decision is left in fire[] for the compaction.
+constexpr unsigned kNoCut = 0xFFFFFFFFu;  // key of a tile without a cut (never a mean's key)
+
+__global__ __launch_bounds__(1024) void sigma_tile_kernel(
+    const float* __restrict__ sigma, const int* __restrict__ counts_x, int* __restrict__ counts,
+    unsigned* __restrict__ gkeys, uint8_t* __restrict__ fire, uint8_t* __restrict__ gate_out,
+    int U, int nb, int k, int sink, float q, int keys_in_lds) {
+  extern __shared__ unsigned skeys[];
+  __shared__ int part[16];
+  const int t = threadIdx.x, l = t & 63, w = t >> 6;
+  unsigned* keys = keys_in_lds ? skeys : gkeys;
+  auto block_sum = [&](int v) {
+    v = wave_sum_int(v);
+    __syncthreads();  // the previous sum's readers are done with part[]
+    if (l == 0) part[w] = v;
+    __syncthreads();
+    int tot = 0;
+    for (int x = 0; x < 16; ++x) tot += part[x];
+    return tot;
+  };
+  int mine = 0;
+  for (int i = t; i < nb; i += 1024) {
+    const int nc = i > 0 ? i - sink : 0;
+    unsigned key = kNoCut;
+    if (nc > k) {
+      float sum = 0.f;
+      for (int u = 0; u < U; ++u) sum += sigma[(size_t)u * nb + i];
+      key = float_key(sum / (float)U);
+      ++mine;
+    }
+    keys[i] = key;
+  }
+  const int T = block_sum(mine);  // (its barriers also publish keys[])
+  const int r = (int)floor((double)q * (double)T);
+  const int need = T - r;  // keys at or above the (r+1)-th smallest
+  unsigned tq = 0xFFFFFFFFu;  // r >= T: every tile with a cut fires
+  if (need > 0) {
+    tq = 0u;
+    for (int bit = 31; bit >= 0; --bit) {
+      const unsigned x = tq | (1u << bit);
+      int c = 0;
+      for (int i = t; i < nb; i += 1024) c += (keys[i] != kNoCut && keys[i] >= x) ? 1 : 0;
+      if (block_sum(c) >= need) tq = x;
+    }
+  }
+  for (int i = t; i < nb; i += 1024) fire[i] = (keys[i] != kNoCut && keys[i] < tq) ? 1 : 0;
+  const int rows = U * nb;
+  for (int row = t; row < rows; row += 1024) {
+    const unsigned key = keys[row % nb];
+    const bool f = key != kNoCut && key < tq;
+    if (f) counts[row] += counts_x[row];
+    if (gate_out) gate_out[row] = f ? 1 : 0;
   }
 }
 
@@ -643,7 +801,11 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int* __restrict__ coun
   if (t == 1023) row_ptr[rows] = clampc((int64_t)before + x);
 }
 
+// With the sigma gate, rows of fired tiles add their expansion bits (disjoint
+// from the kept bits).
 __global__ __launch_bounds__(256) void compact_kernel(const unsigned long long* __restrict__ mask,
+                                                      const unsigned long long* __restrict__ mask_x,
+                                                      const uint8_t* __restrict__ fire,
                                                       const int32_t* __restrict__ row_ptr,
                                                       int32_t* __restrict__ col_idx, int rows,
                                                       int nb, int nw, int64_t capacity) {
@@ -653,10 +815,12 @@ __global__ __launch_bounds__(256) void compact_kernel(const unsigned long long* 
   const int i = row % nb;
   const int nslots = i / 64 + 1;
   const int64_t base = row_ptr[row];
+  const bool expand = fire != nullptr && fire[i];
   int run = 0;
   const unsigned long long lt = lanemask_lt();
   for (int e = 0; e < nslots; ++e) {
-    const unsigned long long w = mask[(size_t)row * nw + e];
+    const unsigned long long w =
+        mask[(size_t)row * nw + e] | (expand ? mask_x[(size_t)row * nw + e] : 0ull);
     if ((w >> l) & 1ull) {
       const int64_t pos = base + run + __popcll(w & lt);
       if (pos < capacity) col_idx[pos] = e * 64 + l;
@@ -669,7 +833,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
 
-SelectWorkspace select_workspace_layout(const Shape& sh, bool export_scores) {
+SelectWorkspace select_workspace_layout(const Shape& sh, bool export_scores, bool sigma_gate) {
   SelectWorkspace w;
   const size_t rows = (size_t)sh.U() * sh.nb;
   const size_t nw = (size_t)(sh.nb + 63) / 64;
@@ -680,6 +844,19 @@ SelectWorkspace select_workspace_layout(const Shape& sh, bool export_scores) {
   off += align256(rows * nw * sizeof(unsigned long long));
   w.counts_off = off;
   off += align256(rows * sizeof(int));
+  w.sigma_off = w.mask_x_off = w.counts_x_off = w.keys_off = w.fire_off = off;
+  if (sigma_gate) {
+    w.sigma_off = off;
+    off += align256(rows * sizeof(float));
+    w.mask_x_off = off;
+    off += align256(rows * nw * sizeof(unsigned long long));
+    w.counts_x_off = off;
+    off += align256(rows * sizeof(int));
+    w.keys_off = off;
+    off += align256((size_t)sh.nb * sizeof(unsigned));
+    w.fire_off = off;
+    off += align256((size_t)sh.nb);
+  }
   w.total = off;
   return w;
 }
@@ -689,7 +866,8 @@ hipError_t launch_score_select(const Shape& sh, const SelectConfig& cfg, const f
                                const float* k_radius, int32_t* row_ptr, int32_t* col_idx,
                                int64_t col_capacity, float* scores_out, float* bound_out,
                                uint8_t* gate_out, void* workspace, hipStream_t stream) {
-  const SelectWorkspace w = select_workspace_layout(sh, scores_out != nullptr);
+  const bool sig = cfg.gate == 2 && cfg.top_k > 0;
+  const SelectWorkspace w = select_workspace_layout(sh, scores_out != nullptr, cfg.gate == 2);
   unsigned char* ws = (unsigned char*)workspace;
   float* scores = scores_out ? scores_out : (float*)(ws + w.scores_off);
   unsigned long long* mask = (unsigned long long*)(ws + w.mask_off);
@@ -726,21 +904,32 @@ hipError_t launch_score_select(const Shape& sh, const SelectConfig& cfg, const f
   a.use_b = cfg.rescue_fraction > 0.0 ? 1 : 0;
   a.use_p = cfg.mass_threshold > 0.0f ? 1 : 0;
   a.per_wave_floats = nw * 64 * (1 + a.use_b + a.use_p);
+  a.sigma = sig ? (float*)(ws + w.sigma_off) : nullptr;
+  a.mask_x = sig ? (unsigned long long*)(ws + w.mask_x_off) : nullptr;
+  a.counts_x = sig ? (int*)(ws + w.counts_x_off) : nullptr;
   // register form for rows up to 64*SPL = 4096 blocks (8192 with the top-k and
   // gate branches only), LDS form beyond
   const bool topk_only = !a.use_b && !a.use_p;
   const int spl = nw <= 1 ? 1 : nw <= 2 ? 2 : nw <= 4 ? 4 : nw <= 8 ? 8 : nw <= 16 ? 16
                   : nw <= 32 ? 32 : nw <= 64 ? 64 : (nw <= 128 && topk_only) ? 128 : 0;
   const dim3 rg((rows + 3) / 4), rb(256);
+#define BSA_SELECT_REG(N, F)                                                               \
+  case N:                                                                                  \
+    if (sig)                                                                               \
+      hipLaunchKernelGGL((select_reg_kernel<N, F, true>), rg, rb, 0, stream, a);           \
+    else                                                                                   \
+      hipLaunchKernelGGL((select_reg_kernel<N, F, false>), rg, rb, 0, stream, a);          \
+    break;
   switch (spl) {
-    case 1: hipLaunchKernelGGL((select_reg_kernel<1, true>), rg, rb, 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((select_reg_kernel<2, true>), rg, rb, 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((select_reg_kernel<4, true>), rg, rb, 0, stream, a); break;
-    case 8: hipLaunchKernelGGL((select_reg_kernel<8, true>), rg, rb, 0, stream, a); break;
-    case 16: hipLaunchKernelGGL((select_reg_kernel<16, true>), rg, rb, 0, stream, a); break;
-    case 32: hipLaunchKernelGGL((select_reg_kernel<32, true>), rg, rb, 0, stream, a); break;
-    case 64: hipLaunchKernelGGL((select_reg_kernel<64, true>), rg, rb, 0, stream, a); break;
-    case 128: hipLaunchKernelGGL((select_reg_kernel<128, false>), rg, rb, 0, stream, a); break;
+    BSA_SELECT_REG(1, true)
+    BSA_SELECT_REG(2, true)
+    BSA_SELECT_REG(4, true)
+    BSA_SELECT_REG(8, true)
+    BSA_SELECT_REG(16, true)
+    BSA_SELECT_REG(32, true)
+    BSA_SELECT_REG(64, true)
+    BSA_SELECT_REG(128, false)
+#undef BSA_SELECT_REG
     default: {
       const size_t per_wave_bytes = (size_t)a.per_wave_floats * sizeof(float);
       int waves = (int)(65536 / per_wave_bytes);
@@ -752,12 +941,23 @@ hipError_t launch_score_select(const Shape& sh, const SelectConfig& cfg, const f
   e = hipGetLastError();
   if (e != hipSuccess) return e;
 
+  uint8_t* fire = nullptr;
+  if (sig) {
+    fire = ws + w.fire_off;
+    const int in_lds = nb <= 8192 ? 1 : 0;  // 32 KiB of keys
+    hipLaunchKernelGGL(sigma_tile_kernel, dim3(1), dim3(1024), in_lds ? nb * sizeof(unsigned) : 0,
+                       stream, a.sigma, a.counts_x, counts, (unsigned*)(ws + w.keys_off), fire,
+                       gate_out, U, nb, cfg.top_k, cfg.force_sink, cfg.gate_threshold, in_lds);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }  // (with the top-k branch off the select kernel writes gate_out = 0 itself)
+
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, stream, counts, row_ptr, rows,
                      col_capacity);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(compact_kernel, dim3((rows + 3) / 4), dim3(256), 0, stream, mask, row_ptr,
-                     col_idx, rows, nb, nw, col_capacity);
+  hipLaunchKernelGGL(compact_kernel, dim3((rows + 3) / 4), dim3(256), 0, stream, mask, a.mask_x,
+                     fire, row_ptr, col_idx, rows, nb, nw, col_capacity);
   return hipGetLastError();
 }
 

@@ -73,7 +73,7 @@ typedef enum {
 
 typedef enum { BSA_BF16 = 0, BSA_FP8_E4M3 = 1 } bsa_dtype;
 typedef enum { BSA_SEL_PER_QHEAD = 0, BSA_SEL_PER_GROUP = 1 } bsa_granularity;
-typedef enum { BSA_GATE_NONE = 0, BSA_GATE_TOP12_GAP = 1 } bsa_gate;
+typedef enum { BSA_GATE_NONE = 0, BSA_GATE_TOP12_GAP = 1, BSA_GATE_SIGMA_CUT = 2 } bsa_gate;
 
 /* Shape of one prefill layer. */
 typedef struct {
@@ -94,7 +94,8 @@ typedef struct {
   int32_t top_k;            /* k >= 0; 0 switches the top-k branch off          */
   int32_t force_sink;       /* 0/1: also force block 0                          */
   int32_t gate;             /* bsa_gate; applies to the top-k branch            */
-  float gate_threshold;     /* theta in (0, 1]: fires when p(0)-p(1) < theta   */
+  float gate_threshold;     /* in (0, 1]: theta for BSA_GATE_TOP12_GAP, the     */
+                            /* percentile level q for BSA_GATE_SIGMA_CUT        */
   int32_t gate_factor;      /* rho >= 1: a fired row keeps rho*k                */
   float score_temperature;  /* tau > 0 in softmax(tau * s) (gate and mass)     */
   float mass_threshold;     /* mu in [0, 1]; 0 switches the base branch off    */
@@ -147,6 +148,15 @@ size_t bsa_score_select_workspace_size(const bsa_problem* problem,
  *   top-k  : the first k of C_i; when gate == BSA_GATE_TOP12_GAP, |C_i| >= 2 and
  *            p(0) - p(1) < theta, the first rho*k instead (same page, "The
  *            Solution" and Methodology step 5);
+ *            when gate == BSA_GATE_SIGMA_CUT the decision is per query block
+ *            (tile) over the whole call, taken as one layer (same page,
+ *            Methodology steps 3-5): a row with a cut (|C_i| > k) has
+ *            sigma = (s(k-1) - s(k)) / (s(0) - s(k)) over its candidate scores
+ *            sorted descending (0 when s(0) = s(k)); tile i's signal is the mean
+ *            of sigma over the U units; with T tiles that have a cut, tile i
+ *            fires when at most floor(q * T) of them (q = gate_threshold, the
+ *            product in double) have a mean <= its own; every row of a fired
+ *            tile keeps the first rho*k;
  *   base   : the shortest prefix of C_i whose mass reaches mu (RBS-Attention base
  *            branch under its own threshold);
  *   rescue : the first ceil(phi * |C_i|) of C_i ranked by the bound
@@ -161,7 +171,8 @@ size_t bsa_score_select_workspace_size(const bsa_problem* problem,
  *   scores_out   out f32 [U, nb, nb] (nullable): the scores the decisions used,
  *                written for j <= i (other entries untouched).
  *   bound_out    out f32 [U, nb, nb] (nullable): the rescue bounds, j <= i.
- *   gate_out     out uint8 [U*nb] (nullable): 1 where the gate fired.
+ *   gate_out     out uint8 [U*nb] (nullable): 1 where the gate fired (for the
+ *                sigma gate: every row of a fired tile).
  *   workspace    device scratch of at least
  *                bsa_score_select_workspace_size(problem, params, scores_out != NULL)
  *                bytes, else BSA_ERR_WORKSPACE.

@@ -7,7 +7,9 @@ Tolerances (written here, derived in the design notes):
   bounds      |b_gpu - b_ref| <= 1e-4 * ||qbar|| * (||kbar|| + r)
   masks       bit-exact: the oracle re-runs selection on the exported fp32 scores
               and bounds; a decision whose float64 quantity is within 1e-5 of its
-              threshold may go either way (counted as ambiguous)
+              threshold may go either way (counted as ambiguous); for the sigma
+              gate the quantity is a tile's head-mean sigma and the threshold the
+              layer's boundary value
   output      bf16 inputs: max-abs <= 2e-2 and mean-abs <= 2e-3;
               E4M3 inputs: max-abs <= 5e-2 and mean-abs <= 5e-3
   lse         |lse_gpu - lse_ref| <= 1e-3
@@ -37,8 +39,7 @@ def params_of(cfg) -> O.SelectParams:
 
 
 def lib_params(cfg):
-    return bsa.make_params(cfg.top_k, cfg.force_sink,
-                           bsa.BSA_GATE_TOP12_GAP if cfg.gate == "top12_gap" else bsa.BSA_GATE_NONE,
+    return bsa.make_params(cfg.top_k, cfg.force_sink, bsa.GATE_CODES[cfg.gate],
                            cfg.gate_threshold, cfg.gate_factor, cfg.score_temperature,
                            cfg.mass_threshold, cfg.rescue_fraction)
 
@@ -130,7 +131,26 @@ class Report:
     mean_abs: float = 0.0
     lse_max: float = 0.0
     kept_blocks: int = 0
+    gate_fired_tiles: int = 0
+    ambiguous_tiles: int = 0
     notes: list = field(default_factory=list)
+
+
+def sigma_boundary_band(sbar: np.ndarray, q: float, delta: float) -> np.ndarray:
+    """Tiles whose decision a float32 evaluation may take the other way.  With
+    r = floor(q*T) the fired tiles are the r smallest head-mean sigmas; a rounding
+    error can only swap a fired and an unfired tile whose values lie within delta
+    of each other across that boundary.  So if the largest fired value a and the
+    smallest unfired value b are more than delta apart, no tile is in doubt;
+    otherwise every tile with a value in [b - delta, a + delta] is."""
+    elig = ~np.isnan(sbar)
+    vals = np.sort(sbar[elig])
+    r = int(math.floor(float(q) * len(vals)))
+    band = np.zeros(sbar.shape[0], dtype=bool)
+    if 0 < r < len(vals) and vals[r] - vals[r - 1] <= delta:
+        x = sbar[elig]
+        band[elig] = (x >= vals[r] - delta) & (x <= vals[r - 1] + delta)
+    return band
 
 
 def check_all(cfg, inp_gpu, run: GpuRun, row_sample=None, unit_sample=None,
@@ -191,6 +211,24 @@ def check_all(cfg, inp_gpu, run: GpuRun, row_sample=None, unit_sample=None,
                 bb = 1e-4 * np.linalg.norm(qbar[u, 0]) * (np.linalg.norm(kbar[0, 0]) + rad[0, 0])
                 assert abs(float(b_gpu[u, i, j]) - bref) <= bb + 1e-30, f"bound ({u},{i},{j})"
 
+    # ---- sigma gate: the per-tile decision over the whole layer, from the exported
+    # scores (every row's sigma is needed, whatever the row sample)
+    tile_opts = None
+    if p.gate == "sigma_cut" and p.top_k > 0:
+        s_all = s_gpu.double().cpu().numpy()
+        sbar, fired64 = O.sigma_gate_tiles(O.sigma_matrix(s_all, p.top_k, p.force_sink),
+                                           p.gate_threshold)
+        del s_all
+        amb = sigma_boundary_band(sbar, p.gate_threshold, AMBIG_DELTA)
+        g = run.gate.reshape(U, nb).astype(bool)
+        assert (g == g[0:1]).all(), "sigma gate: units of one tile disagree"
+        bad = np.nonzero((g[0] != fired64) & ~amb)[0]
+        assert len(bad) == 0, f"sigma gate: tiles {bad[:8]} gpu {g[0][bad[:8]]} vs oracle"
+        tile_opts = [((True, False) if amb[i] else (bool(fired64[i]),)) for i in range(nb)]
+        rep.gate_fired_tiles = int(g[0].sum())
+        rep.ambiguous_tiles = int(amb.sum())
+        assert rep.ambiguous_tiles <= max(2, nb // 100), f"{rep.ambiguous_tiles} tiles in doubt"
+
     # ---- masks: oracle re-runs selection on the exported fp32 scores and bounds
     if row_sample is None:
         rows = [(u, i) for u in units for i in range(nb)]
@@ -204,7 +242,8 @@ def check_all(cfg, inp_gpu, run: GpuRun, row_sample=None, unit_sample=None,
         kept_gpu[(u, i)] = kept
         srow = s_gpu[u, i, : i + 1].double().cpu().numpy()
         brow = None if b_gpu is None else b_gpu[u, i, : i + 1].double().cpu().numpy()
-        sets, amb = O.acceptable_row_sets(i, srow, brow, p, AMBIG_DELTA)
+        sets, amb = O.acceptable_row_sets(i, srow, brow, p, AMBIG_DELTA,
+                                          tile_opts[i] if tile_opts else (False,))
         fired = bool(run.gate[r])
         assert (kept, fired) in [(k_, f_ if p.gate != "none" else False) for k_, f_ in sets] or \
             (p.gate == "none" and any(k_ == kept for k_, _ in sets)), \

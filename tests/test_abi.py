@@ -74,7 +74,8 @@ def test_pool_requires_pointers_and_fp8_scales(lib):
 @pytest.mark.parametrize("kw", [dict(top_k=-1), dict(gate=5), dict(gate=1, gate_threshold=0.0),
                                 dict(gate=1, gate_factor=0), dict(score_temperature=0.0),
                                 dict(mass_threshold=1.5), dict(rescue_fraction=-0.1),
-                                dict(force_sink=2)])
+                                dict(force_sink=2), dict(gate=3), dict(gate=2, gate_threshold=0.0),
+                                dict(gate=2, gate_threshold=1.5), dict(gate=2, gate_factor=0)])
 def test_select_rejects_bad_params(lib, kw):
     p = _prob()
     d = dict(top_k=4, force_sink=1)
@@ -129,6 +130,28 @@ def test_capacity_bound_covers_any_selection(lib):
                 kept, _ = O.select_row(i, sc, sc + rng.uniform(0, 2, size=i + 1), op)
                 total += len(kept)
         assert total <= bound
+
+
+def test_sigma_gate_bound_and_workspace(lib):
+    """With q = 1 every tile that has a cut fires, so every row keeps min(rho*k, |C|)
+    plus its forced blocks: the oracle's total then equals the capacity bound.  The
+    sigma gate's workspace adds its per-row and per-tile arrays."""
+    from oracle import bsa_oracle as O
+    rng = np.random.default_rng(1)
+    nb, U = 23, 3
+    p = _prob(seq_len=nb * 128 - 7, num_q_heads=U, num_kv_heads=1)
+    s = bsa.make_params(top_k=4, force_sink=1, gate=bsa.BSA_GATE_SIGMA_CUT, gate_threshold=1.0,
+                        gate_factor=2)
+    bound = lib.bsa_csr_capacity_bound(ctypes.byref(p), ctypes.byref(s))
+    op = O.SelectParams(top_k=4, force_sink=True, gate="sigma_cut", gate_threshold=1.0,
+                        gate_factor=2).as_library_precision()
+    kept, fired = O.select(rng.normal(size=(U, nb, nb)), None, op)
+    assert sum(len(r) for unit in kept for r in unit) == bound
+    assert fired[:, 6:].all() and not fired[:, :6].any()  # a cut needs i - 1 > 4
+    s0 = bsa.make_params(top_k=4, force_sink=1)
+    w0 = lib.bsa_score_select_workspace_size(ctypes.byref(p), ctypes.byref(s0), 0)
+    w2 = lib.bsa_score_select_workspace_size(ctypes.byref(p), ctypes.byref(s), 0)
+    assert w2 >= w0 + U * nb * (4 + 8 + 4) + nb * 5
 
 
 def test_attention_rejects_bad_arguments(lib):

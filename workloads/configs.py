@@ -41,7 +41,7 @@ class WorkloadConfig:
     # selection
     top_k: int = 0
     force_sink: bool = False
-    gate: str = "none"  # "none" or "top12_gap"
+    gate: str = "none"  # "none", "top12_gap" or "sigma_cut"
     gate_threshold: float = 0.05
     gate_factor: int = 2
     score_temperature: float = 1.0
@@ -110,8 +110,16 @@ CONFIGS = [
 # block) scales), the precision RBS-Attention reports its 128K results in
 # (RBS-Attention article, fourth paragraph).  Same seeds and structure as
 # dual128k, quantised.
+#
+# The 64K gated workload under the page's own gate instead of the lay summary's:
+# per (tile, head) the normalised cut margin sigma, its mean over heads per tile,
+# and expansion to rho*k of the tiles in the lowest q = 0.30 of the layer's
+# distribution ("Uncertainty-gated selection for block-sparse attention",
+# technical summary, Methodology steps 3-5; q matches the fraction of query
+# blocks the generator plants near-ties in).  Same seeds and inputs as gated64k.
 EXTRA_CONFIGS = [
     dataclasses.replace(CONFIGS[3], name="dual128k_fp8", dtype="fp8"),
+    dataclasses.replace(CONFIGS[2], name="sigma64k", gate="sigma_cut", gate_threshold=0.30),
 ]
 
 
