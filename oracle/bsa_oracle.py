@@ -23,6 +23,12 @@ The method, as the source pages describe it:
     averaged over heads per tile; tiles whose mean falls in the lowest part of
     the layer's empirical distribution expand to rho*k (same page, Methodology
     steps 3-5).
+  * Quest backbone: each key block is summarised by the coordinate-wise minimum
+    and maximum of its keys; a query row's score against the block is the
+    largest q.k over that box, sum_d max(q_d kmin_d, q_d kmax_d), an upper
+    bound on every key of the block; a tile scores a block by the maximum over
+    its query rows (same page, Methodology steps 1-2: per-coordinate upper
+    bounds as the second backbone, tile score = max over the tile's rows).
   * RBS-Attention: a base branch keeps centroid-relevant blocks under its own
     threshold, a rescue branch flags blocks whose centroid may underestimate
     them using a per-(prompt, layer, head) key-block radius; the two masks are
@@ -56,7 +62,7 @@ __all__ = [
     "SelectParams", "decode_bf16", "decode_e4m3", "dequantize", "decode_inputs",
     "pool_queries", "pool_keys", "block_scores", "rescue_bounds", "candidate_sets",
     "descending_order", "top_k", "gate_gap", "sigma_cut_margin", "sigma_gate_tiles",
-    "sigma_matrix", "tile_gate", "mass_prefix_length", "rescue_count",
+    "sigma_matrix", "tile_gate", "key_block_bounds", "quest_row_bound", "quest_scores", "mass_prefix_length", "rescue_count",
     "select_row", "acceptable_row_sets", "select", "to_csr", "from_csr",
     "attend", "block_tokens", "attention_unit", "attention", "dense_causal_attention", "block_of", "unit_of_head",
     "kv_of_unit",
@@ -200,6 +206,58 @@ def pool_keys(K: np.ndarray, B: int):
             kbar[g, j] = c
             radius[g, j] = np.sqrt(((rows - c) ** 2).sum(axis=1)).max()
     return kbar, radius
+
+
+# ----------------------------------------------------------------------------
+# step 1b: the Quest backbone's key-block summaries
+
+def key_block_bounds(K: np.ndarray, B: int):
+    """Coordinate-wise minimum and maximum of each key block ("Uncertainty-gated
+    selection ...", technical summary, Methodology step 1: Quest's K-min/K-max).
+
+    kmin[g, j, d] = min over keys t of block j of K[t, g, d]; kmax likewise.
+    Returns (kmin, kmax), each [Hkv, nb, D]; a ragged last block uses its rows.
+    """
+    S, Hkv, D = K.shape
+    ranges = _block_ranges(S, B)
+    kmin = np.zeros((Hkv, len(ranges), D))
+    kmax = np.zeros((Hkv, len(ranges), D))
+    for j, (t0, t1) in enumerate(ranges):
+        kmin[:, j] = K[t0:t1].min(axis=0)
+        kmax[:, j] = K[t0:t1].max(axis=0)
+    return kmin, kmax
+
+
+def quest_row_bound(q_rows: np.ndarray, kmin: np.ndarray, kmax: np.ndarray) -> np.ndarray:
+    """Largest q.k over the box kmin <= k <= kmax, for every query row and block:
+    coordinate d contributes max(q_d * kmin_d, q_d * kmax_d).  [n_rows, n_blocks]."""
+    lo = q_rows[:, None, :] * kmin[None, :, :]
+    hi = q_rows[:, None, :] * kmax[None, :, :]
+    return np.maximum(lo, hi).sum(axis=-1)
+
+
+def quest_scores(Q: np.ndarray, kmin: np.ndarray, kmax: np.ndarray, B: int, num_kv_heads: int,
+                 granularity: str) -> np.ndarray:
+    """Tile scores of the Quest backbone with per-row scoring (same page,
+    Methodology step 2: a tile's score is the maximum over its rows).
+
+    s[u, i, j] = max over the query rows t of tile i, and over the heads of unit u,
+    of quest_row_bound(Q[t, h], kmin[g, j], kmax[g, j]), for j <= i; NaN above
+    the diagonal (g = the unit's kv head).
+    """
+    S, Hq, D = Q.shape
+    ranges = _block_ranges(S, B)
+    nb = len(ranges)
+    G = Hq // num_kv_heads
+    U = Hq if granularity == "qhead" else num_kv_heads
+    s = np.full((U, nb, nb), np.nan)
+    for u in range(U):
+        heads = [u] if granularity == "qhead" else list(range(u * G, (u + 1) * G))
+        g = kv_of_unit(u, Hq, num_kv_heads, granularity)
+        for i, (t0, t1) in enumerate(ranges):
+            rows = Q[t0:t1, heads, :].reshape(-1, D)
+            s[u, i, : i + 1] = quest_row_bound(rows, kmin[g, : i + 1], kmax[g, : i + 1]).max(axis=0)
+    return s
 
 
 # ----------------------------------------------------------------------------

@@ -160,6 +160,77 @@ def test_rescue_bound_cauchy_schwarz_invariant():
     assert np.allclose(b2[m], s2[m], atol=1e-12)
 
 
+# ---------------------------------------------------------------- Quest backbone
+
+def test_quest_bound_is_the_box_maximum_by_corner_enumeration():
+    # the largest of a linear function over a box sits at one of its 2^D corners
+    rng = np.random.default_rng(50)
+    for _ in range(50):
+        D = int(rng.integers(1, 7))
+        a, b = rng.normal(size=D), rng.normal(size=D)
+        kmin, kmax = np.minimum(a, b), np.maximum(a, b)
+        q = rng.normal(size=(3, D))
+        got = O.quest_row_bound(q, kmin[None], kmax[None])[:, 0]
+        corners = np.array(list(itertools.product(*zip(kmin, kmax))))
+        assert np.allclose(got, (q @ corners.T).max(axis=1), rtol=0, atol=1e-12)
+
+
+def test_quest_bound_sign_picks_the_right_end():
+    # q = -e0: the bound uses the minimum of coordinate 0 (-(-2) = 2), not its maximum
+    kmin, kmax = np.array([[-2.0, 0.0]]), np.array([[3.0, 0.0]])
+    assert O.quest_row_bound(np.array([[-1.0, 0.0]]), kmin, kmax)[0, 0] == 2.0
+    assert O.quest_row_bound(np.array([[1.0, 0.0]]), kmin, kmax)[0, 0] == 3.0
+
+
+def test_key_block_bounds_closed_forms():
+    B, D = 4, 3
+    c, a = np.array([1.0, -2.0, 0.5]), np.array([0.5, -1.0, 2.0])
+    K = np.stack([c + a, c - a, c, c + 0.5 * a, c - a])[:, None, :]  # 5 rows: 1 full block + ragged
+    kmin, kmax = O.key_block_bounds(K, B)
+    assert np.array_equal(kmin[0, 0], c - np.abs(a)) and np.array_equal(kmax[0, 0], c + np.abs(a))
+    assert np.array_equal(kmin[0, 1], c - a) and np.array_equal(kmax[0, 1], c - a)
+
+
+def test_quest_scores_upper_bound_every_logit_and_are_tight_on_constant_blocks():
+    rng = np.random.default_rng(51)
+    S, Hq, Hkv, D, B = 7 * 16 - 5, 4, 2, 8, 16
+    Q = rng.normal(size=(S, Hq, D))
+    K = rng.normal(size=(S, Hkv, D))
+    K[2 * B:3 * B, 1] = K[2 * B, 1]  # block 2 of kv head 1: every key the same
+    kmin, kmax = O.key_block_bounds(K, B)
+    for gran in ("qhead", "group"):
+        s = O.quest_scores(Q, kmin, kmax, B, Hkv, gran)
+        U = s.shape[0]
+        G = Hq // Hkv
+        for u in range(U):
+            heads = [u] if gran == "qhead" else list(range(u * G, (u + 1) * G))
+            g = O.kv_of_unit(u, Hq, Hkv, gran)
+            for i in range(s.shape[1]):
+                qi = Q[i * B:(i + 1) * B, heads].reshape(-1, D)
+                for j in range(i + 1):
+                    logits = qi @ K[j * B:(j + 1) * B, g].T
+                    assert s[u, i, j] >= logits.max() - 1e-12
+                    if g == 1 and j == 2:
+                        assert s[u, i, j] == pytest.approx(logits.max(), abs=1e-12)
+                assert np.all(np.isnan(s[u, i, i + 1:]))
+
+
+def test_quest_scores_take_the_row_maximum_and_the_group_maximum():
+    # one loud row in a quiet tile sets the tile's score (a mean would divide it by B)
+    S, D, B = 8, 2, 4
+    Q = np.zeros((S, 2, D))
+    Q[5, 0] = [10.0, 0.0]
+    Q[6, 1] = [0.0, -3.0]
+    K = np.zeros((S, 1, D))
+    K[:, 0] = [1.0, -1.0]
+    kmin, kmax = O.key_block_bounds(K, B)
+    s = O.quest_scores(Q, kmin, kmax, B, 1, "qhead")
+    assert s[0, 1, 0] == 10.0 and s[1, 1, 0] == 3.0 and s[0, 0, 0] == 0.0
+    sg = O.quest_scores(Q, kmin, kmax, B, 1, "group")
+    fill = lambda a: np.where(np.isnan(a), -np.inf, a)  # noqa: E731
+    assert sg[0, 1, 0] == 10.0 and np.array_equal(fill(s).max(axis=0), fill(sg[0]))
+
+
 # ---------------------------------------------------------------- selection
 
 def test_top_k_brute_force_with_ties():
