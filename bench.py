@@ -53,24 +53,40 @@ def dense_causal_flops(cfg) -> float:
 
 def pool_select_bytes(cfg, nnz: int) -> float:
     """Algorithmic HBM bytes of pool + score/select: Q and K read once (plus E4M3
-    scales), centroids/norms/radii written and read once, CSR written."""
+    scales), the block summaries written and read once (centroids/norms/radii, or
+    the Quest key bounds), CSR written."""
     S, Hq, Hkv, D, nb, U = (cfg.seq_len, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim,
                             cfg.num_blocks, cfg.num_units)
     es = 1 if cfg.dtype == "fp8" else 2
     b = S * (Hq + Hkv) * D * es
     if cfg.dtype == "fp8":
         b += (Hq + Hkv) * nb * 4
-    b += 2 * ((U * nb * D + Hkv * nb * D) * 4 + (U * nb + Hkv * nb) * 4)
+    if cfg.backbone == "quest":
+        b += 2 * (2 * Hkv * nb * D * 4)
+    else:
+        b += 2 * ((U * nb * D + Hkv * nb * D) * 4 + (U * nb + Hkv * nb) * 4)
     b += 4 * (U * nb + 1) + 4 * nnz
     return float(b)
 
 
+def quest_flops(cfg) -> float:
+    """Algorithmic FLOPs of the Quest tile scores: per query row of every head and
+    every causal key block, sum_d max(q_d kmin_d, q_d kmax_d) as 2D multiply-adds."""
+    S, B, nb = cfg.seq_len, cfg.block_size, cfg.num_blocks
+    rows_by_tile = sum(min(B, S - i * B) * (i + 1) for i in range(nb))
+    return float(cfg.num_q_heads * rows_by_tile * 4 * cfg.head_dim)
+
+
 def pool_bytes(cfg) -> float:
     """Algorithmic HBM bytes of the pool stage alone: Q and K read once (plus E4M3
-    scales), centroids, norms and radii written once."""
+    scales), centroids, norms and radii written once; on the Quest backbone K read
+    once and its bounds written."""
     S, Hq, Hkv, D, nb, U = (cfg.seq_len, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim,
                             cfg.num_blocks, cfg.num_units)
     es = 1 if cfg.dtype == "fp8" else 2
+    if cfg.backbone == "quest":
+        return float(S * Hkv * D * es + (Hkv * nb * 4 if cfg.dtype == "fp8" else 0)
+                     + 2 * Hkv * nb * D * 4)
     b = S * (Hq + Hkv) * D * es
     if cfg.dtype == "fp8":
         b += (Hq + Hkv) * nb * 4
@@ -136,14 +152,30 @@ def cpu_baseline(cfg, inp, sel_rows, budget_s: float = 15.0):
                        cfg.rescue_fraction).as_library_precision()
     rng = np.random.default_rng(0)
     kv = 0
+    fp8 = cfg.dtype == "fp8"
+    quest = cfg.backbone == "quest"
+
+    def host_raw(t):
+        t = t.cpu()
+        return t.numpy() if fp8 else t.view(torch.int16).numpy().view(np.uint16)
+
+    def decode(raw, scale):  # raw [rows, H, D] -> float64, with [H, nb] scales for E4M3
+        return O.dequantize(raw, scale, B) if fp8 else O.decode_bf16(raw)
+
     t_host = time.perf_counter()
-    kraw = inp.k[:, kv].cpu().view(torch.int16).numpy().view(np.uint16)
-    vraw = inp.v[:, kv].cpu().view(torch.int16).numpy().view(np.uint16)
+    kraw = host_raw(inp.k[:, kv:kv + 1])
+    vraw = host_raw(inp.v[:, kv:kv + 1])
+    ks = inp.k_scale[kv:kv + 1].cpu().numpy().astype(np.float64) if fp8 else None
+    vs = inp.v_scale[kv:kv + 1].cpu().numpy().astype(np.float64) if fp8 else None
+    qs_all = inp.q_scale.cpu().numpy().astype(np.float64) if fp8 else None
     copy_s = time.perf_counter() - t_host
     t0 = time.perf_counter()
-    K = O.decode_bf16(kraw)[:, None, :]
-    V = O.decode_bf16(vraw)[:, None, :]
-    kbar, rad = O.pool_keys(K, B)
+    K = decode(kraw, ks)
+    V = decode(vraw, vs)
+    if quest:
+        kmin, kmax = O.key_block_bounds(K, B)
+    else:
+        kbar, rad = O.pool_keys(K, B)
     flops = 0.0
     units = 0
     heads = [h for h in range(Hq) if h // G == kv]
@@ -151,11 +183,19 @@ def cpu_baseline(cfg, inp, sel_rows, budget_s: float = 15.0):
         i = int(rng.integers(nb))
         h = heads[int(rng.integers(len(heads)))]
         u = h if gran == "qhead" else kv
-        q_rows = inp.q[i * B:min(S, (i + 1) * B)].cpu()
-        qh = O.decode_bf16(q_rows.view(torch.int16).numpy().view(np.uint16))
-        qbar, qn = O.pool_queries(qh, B, Hkv, gran)
-        s = qbar[u, 0] @ kbar[0, : i + 1].T
-        b = s + qn[u, 0] * rad[0, : i + 1]
+        qh = decode(host_raw(inp.q[i * B:min(S, (i + 1) * B)]),
+                    None if qs_all is None else qs_all[:, i:i + 1])
+        hs = [h] if gran == "qhead" else heads
+        if quest:
+            rows = qh[:, hs, :].reshape(-1, D)
+            s = O.quest_row_bound(rows, kmin[0, : i + 1], kmax[0, : i + 1]).max(axis=0)
+            b = None
+        else:
+            qbar, qn = O.pool_queries(qh, B, Hkv, gran)
+            s = qbar[u, 0] @ kbar[0, : i + 1].T
+            b = s + qn[u, 0] * rad[0, : i + 1]
+        if p.gate == "sigma_cut":
+            O.sigma_cut_margin(s, O.candidate_sets(i, p.force_sink)[1], p.top_k)
         kept, _ = O.select_row(i, s, b, p)
         keys = O.block_tokens(kept, B, S)
         O.attend(qh[:, h], i * B + np.arange(qh.shape[0]), K[keys, 0], V[keys, 0], keys,
@@ -173,7 +213,12 @@ def cpu_baseline(cfg, inp, sel_rows, budget_s: float = 15.0):
         cores = len(os.sched_getaffinity(0))
     return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": (f"{units} random (query block, head) rows of kv head 0 at S={S}: "
-                       f"pool + score vs all key blocks + select + attention, plus pooling of "
+                       + ("Quest row bounds vs all key blocks" if quest
+                          else "pool + score vs all key blocks")
+                       + " + select"
+                       + (" (per-row sigma; the layer-wide tile percentile not sampled)"
+                          if p.gate == "sigma_cut" else "")
+                       + f" + attention, plus {'bounds' if quest else 'pooling'} of "
                        f"kv head 0's {nb} key blocks, {el:.1f} s of float64 NumPy "
                        f"(host copy {copy_s:.1f} s excluded)"),
             "seconds": round(el, 2)}
@@ -280,9 +325,14 @@ def main(argv=None) -> int:
                              cfg.gate_threshold, cfg.gate_factor, cfg.score_temperature,
                              cfg.mass_threshold, cfg.rescue_fraction)
     rescue = cfg.rescue_fraction > 0
-    pool = bsa.bsa_pool(problem, inp.q, inp.k, inp.q_scale, inp.k_scale, want_norm=rescue,
-                        want_radius=rescue)
-    bufs = bsa.SelectBuffers(problem, params, dev, export=False)
+    quest = cfg.backbone == "quest"
+    if quest:
+        kb = bsa.bsa_pool_key_bounds(problem, inp.k, inp.k_scale)
+        qbufs = bsa.QuestBuffers(problem, dev)
+    else:
+        pool = bsa.bsa_pool(problem, inp.q, inp.k, inp.q_scale, inp.k_scale, want_norm=rescue,
+                            want_radius=rescue)
+    bufs = bsa.SelectBuffers(problem, params, dev, export=False, given_scores=quest)
     out = torch.empty(cfg.seq_len, cfg.num_q_heads, cfg.head_dim, dtype=torch.bfloat16, device=dev)
     lse = torch.empty(cfg.num_q_heads, cfg.seq_len, dtype=torch.float32, device=dev)
     scale = 1.0 / math.sqrt(cfg.head_dim)
@@ -290,10 +340,19 @@ def main(argv=None) -> int:
     def step(ev=None):
         if ev:
             ev[0].record()
-        bsa.bsa_pool(problem, inp.q, inp.k, inp.q_scale, inp.k_scale, out=pool)
+        if quest:
+            bsa.bsa_pool_key_bounds(problem, inp.k, inp.k_scale, out=kb)
+        else:
+            bsa.bsa_pool(problem, inp.q, inp.k, inp.q_scale, inp.k_scale, out=pool)
         if ev:
             ev[1].record()
-        sel = bsa.bsa_score_select(problem, params, pool, buffers=bufs)
+        if quest:
+            sc = bsa.bsa_quest_scores(problem, inp.q, kb[0], kb[1], inp.q_scale, buffers=qbufs)
+            if ev:
+                ev[4].record()
+            sel = bsa.bsa_select_scores(problem, params, sc, buffers=bufs)
+        else:
+            sel = bsa.bsa_score_select(problem, params, pool, buffers=bufs)
         if ev:
             ev[2].record()
         bsa.bsa_attention_fwd(problem, inp.q, inp.k, inp.v, sel.row_ptr, sel.col_idx, scale,
@@ -306,7 +365,7 @@ def main(argv=None) -> int:
         step()
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -361,10 +420,18 @@ def main(argv=None) -> int:
         "kept_tflop": round(kept_flops / 1e12, 4),
         "density": round(nnz / causal_blocks, 5),
         "dense_causal_tflop": round(dense / 1e12, 3),
+        "backbone": cfg.backbone,
         "pool_select": {"algorithmic_gb": round(ps_bytes / 1e9, 4),
                         "gbs": round(ps_bytes / (ps_ms * 1e-3) / 1e9, 1),
                         "frac_hbm": round(ps_bytes / (ps_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
     }
+    if quest:
+        qs_ms = float(np.mean([e[1].elapsed_time(e[4]) for e in evs]))
+        qf = quest_flops(cfg)
+        res["quest_scores"] = {"ms": round(qs_ms, 4), "tflop": round(qf / 1e12, 4),
+                               "tflops": round(qf / (qs_ms * 1e-3) / 1e12, 2),
+                               "frac_bf16_peak": round(qf / (qs_ms * 1e-3) / 1e12
+                                                       / PEAK_BF16_TFLOPS, 4)}
     copy_gbs = copy_bandwidth(torch, dev)
     pb = pool_bytes(cfg)
     res["pool_select"]["copy_gbs"] = round(copy_gbs, 1)

@@ -81,6 +81,11 @@ def load_library(path: str = LIB_PATH):
         "bsa_score_select_workspace_size": ([PP, PS, ctypes.c_int], SZ),
         "bsa_score_select": ([PP, PS, P, P, P, P, P, P, I64, P, P, P, P, SZ, P], ctypes.c_int),
         "bsa_attention_fwd": ([PP, P, P, P, P, P, P, P, P, F, P, P, P], ctypes.c_int),
+        "bsa_pool_key_bounds": ([PP, P, P, P, P, P], ctypes.c_int),
+        "bsa_quest_scores_workspace_size": ([PP], SZ),
+        "bsa_quest_scores": ([PP, P, P, P, P, P, P, SZ, P], ctypes.c_int),
+        "bsa_select_scores_workspace_size": ([PP, PS], SZ),
+        "bsa_select_scores": ([PP, PS, P, P, P, I64, P, P, SZ, P], ctypes.c_int),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(L, name)
@@ -171,9 +176,11 @@ def bsa_pool(problem: Problem, q, k, q_scale=None, k_scale=None, want_norm=True,
 
 
 class SelectBuffers:
-    """Device buffers for bsa_score_select sized once for a (problem, params) pair."""
+    """Device buffers for bsa_score_select (or, with given_scores, bsa_select_scores)
+    sized once for a (problem, params) pair."""
 
-    def __init__(self, problem: Problem, params: SelectParams, device, export=False):
+    def __init__(self, problem: Problem, params: SelectParams, device, export=False,
+                 given_scores=False):
         import torch
         L = load_library()
         rows = L.bsa_num_select_rows(ctypes.byref(problem))
@@ -183,17 +190,21 @@ class SelectBuffers:
                                       None, None, None, None, 0, None, None, None, None, 0, None))
         nb = L.bsa_num_blocks(ctypes.byref(problem))
         U = rows // max(nb, 1)
-        ws = L.bsa_score_select_workspace_size(ctypes.byref(problem), ctypes.byref(params),
-                                               int(export))
+        if given_scores:
+            ws = L.bsa_select_scores_workspace_size(ctypes.byref(problem), ctypes.byref(params))
+        else:
+            ws = L.bsa_score_select_workspace_size(ctypes.byref(problem), ctypes.byref(params),
+                                                   int(export))
         self.row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=device)
         self.col_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=device)
         self.capacity = cap
         self.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=device)
         self.scores = self.bounds = self.gate = None
         if export:
-            self.scores = torch.empty(U, nb, nb, dtype=torch.float32, device=device)
-            if params.rescue_fraction > 0:
-                self.bounds = torch.empty(U, nb, nb, dtype=torch.float32, device=device)
+            if not given_scores:
+                self.scores = torch.empty(U, nb, nb, dtype=torch.float32, device=device)
+                if params.rescue_fraction > 0:
+                    self.bounds = torch.empty(U, nb, nb, dtype=torch.float32, device=device)
             self.gate = torch.empty(rows, dtype=torch.uint8, device=device)
 
 
@@ -208,6 +219,62 @@ def bsa_score_select(problem: Problem, params: SelectParams, pool: PoolResult, e
                               _ptr(b.bounds), _ptr(b.gate), _ptr(b.workspace),
                               b.workspace.numel(), _stream(dev)))
     return Selection(b.row_ptr, b.col_idx, None, b.scores, b.bounds, b.gate)
+
+
+def bsa_pool_key_bounds(problem: Problem, k, k_scale=None, out=None):
+    """(k_min, k_max), each f32 [Hkv, nb, D]: the coordinate-wise extremes of every key block."""
+    import torch
+    L = load_library()
+    nb = L.bsa_num_blocks(ctypes.byref(problem))
+    if nb < 0:
+        _check(L.bsa_pool_key_bounds(ctypes.byref(problem), None, None, None, None, None))
+    if out is None:
+        shape = (problem.num_kv_heads, nb, problem.head_dim)
+        out = (torch.empty(shape, dtype=torch.float32, device=k.device),
+               torch.empty(shape, dtype=torch.float32, device=k.device))
+    _check(L.bsa_pool_key_bounds(ctypes.byref(problem), _ptr(_u8(k)), _ptr(k_scale), _ptr(out[0]),
+                                 _ptr(out[1]), _stream(k.device)))
+    return out
+
+
+class QuestBuffers:
+    """Scores [U, nb, nb] and the repacking workspace of bsa_quest_scores."""
+
+    def __init__(self, problem: Problem, device):
+        import torch
+        L = load_library()
+        nb = L.bsa_num_blocks(ctypes.byref(problem))
+        rows = L.bsa_num_select_rows(ctypes.byref(problem))
+        if nb < 0 or rows < 0:
+            _check(L.bsa_quest_scores(ctypes.byref(problem), None, None, None, None, None, None, 0,
+                                      None))
+        U = rows // max(nb, 1)
+        ws = L.bsa_quest_scores_workspace_size(ctypes.byref(problem))
+        self.scores = torch.empty(U, nb, nb, dtype=torch.float32, device=device)
+        self.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=device)
+
+
+def bsa_quest_scores(problem: Problem, q, k_min, k_max, q_scale=None,
+                     buffers: QuestBuffers | None = None):
+    """Quest tile scores f32 [U, nb, nb] (entries j <= i written)."""
+    L = load_library()
+    b = buffers or QuestBuffers(problem, q.device)
+    _check(L.bsa_quest_scores(ctypes.byref(problem), _ptr(_u8(q)), _ptr(q_scale), _ptr(k_min),
+                              _ptr(k_max), _ptr(b.scores), _ptr(b.workspace), b.workspace.numel(),
+                              _stream(q.device)))
+    return b.scores
+
+
+def bsa_select_scores(problem: Problem, params: SelectParams, scores, export=False,
+                      buffers: SelectBuffers | None = None) -> Selection:
+    """Selection on given scores; with export the gate flags are returned too."""
+    L = load_library()
+    dev = scores.device
+    b = buffers or SelectBuffers(problem, params, dev, export, given_scores=True)
+    _check(L.bsa_select_scores(ctypes.byref(problem), ctypes.byref(params), _ptr(scores),
+                               _ptr(b.row_ptr), _ptr(b.col_idx), b.capacity, _ptr(b.gate),
+                               _ptr(b.workspace), b.workspace.numel(), _stream(dev)))
+    return Selection(b.row_ptr, b.col_idx, None, scores if export else None, None, b.gate)
 
 
 def bsa_attention_fwd(problem: Problem, q, k, v, row_ptr, col_idx, softmax_scale=None,
@@ -226,6 +293,19 @@ def bsa_attention_fwd(problem: Problem, q, k, v, row_ptr, col_idx, softmax_scale
                                _ptr(col_idx), float(softmax_scale), _ptr(out),
                                _ptr(lse) if want_lse else None, _stream(q.device)))
     return out, (lse if want_lse else None)
+
+
+def prefill_quest(q, k, v, block_size: int, params: SelectParams, granularity=BSA_SEL_PER_QHEAD,
+                  q_scale=None, k_scale=None, v_scale=None, softmax_scale=None, export=False):
+    """One layer on the Quest backbone: key bounds -> tile scores -> select -> attention.
+    Returns (out, lse, selection, (k_min, k_max))."""
+    problem = make_problem(q, k, block_size, granularity)
+    bounds = bsa_pool_key_bounds(problem, k, k_scale)
+    scores = bsa_quest_scores(problem, q, bounds[0], bounds[1], q_scale)
+    sel = bsa_select_scores(problem, params, scores, export=export)
+    out, lse = bsa_attention_fwd(problem, q, k, v, sel.row_ptr, sel.col_idx, softmax_scale,
+                                 q_scale, k_scale, v_scale)
+    return out, lse, sel, bounds
 
 
 def prefill(q, k, v, block_size: int, params: SelectParams, granularity=BSA_SEL_PER_QHEAD,

@@ -24,7 +24,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libbsa.so")
 
-SOURCES = ["api.cpp", "pool.hip", "score_select.hip", "attention.hip"]
+SOURCES = ["api.cpp", "pool.hip", "score_select.hip", "quest.hip", "attention.hip"]
 ARCH = os.environ.get("BSA_OFFLOAD_ARCH", "gfx950")
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -114,6 +114,21 @@ int64_t capacity_bound(const bsa::Shape& sh, const bsa_select_params* s) {
   return per_unit * sh.U();
 }
 
+bsa::SelectConfig select_config(const bsa_select_params* params) {
+  bsa::SelectConfig cfg;
+  cfg.top_k = params->top_k;
+  cfg.force_sink = params->force_sink;
+  cfg.gate = params->gate == BSA_GATE_TOP12_GAP ? 1 : params->gate == BSA_GATE_SIGMA_CUT ? 2 : 0;
+  cfg.gate_factor = params->gate_factor;
+  cfg.gate_threshold = params->gate_threshold;
+  cfg.temperature = params->score_temperature;
+  cfg.mass_threshold = params->mass_threshold;
+  cfg.rescue_fraction = params->rescue_fraction;
+  return cfg;
+}
+
+bool misaligned(const void* p) { return ((uintptr_t)p & 15) != 0; }
+
 bsa_status device_status(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(BSA_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
   return ok();
@@ -212,21 +227,97 @@ bsa_status bsa_score_select(const bsa_problem* problem, const bsa_select_params*
           .total;
   if (!workspace || workspace_bytes < need)
     return fail(BSA_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, need);
-  bsa::SelectConfig cfg;
-  cfg.top_k = params->top_k;
-  cfg.force_sink = params->force_sink;
-  cfg.gate = params->gate == BSA_GATE_TOP12_GAP ? 1 : params->gate == BSA_GATE_SIGMA_CUT ? 2 : 0;
-  cfg.gate_factor = params->gate_factor;
-  cfg.gate_threshold = params->gate_threshold;
-  cfg.temperature = params->score_temperature;
-  cfg.mass_threshold = params->mass_threshold;
-  cfg.rescue_fraction = params->rescue_fraction;
+  const bsa::SelectConfig cfg = select_config(params);
   return device_status(
       bsa::launch_score_select(sh, cfg, q_centroid, rescue ? q_norm : nullptr, k_centroid,
                                rescue ? k_radius : nullptr, row_ptr, col_idx, col_capacity,
                                scores_out, rescue ? bound_out : nullptr, gate_out, workspace,
                                (hipStream_t)hip_stream),
       "bsa_score_select launch");
+}
+
+bsa_status bsa_pool_key_bounds(const bsa_problem* problem, const void* k, const float* k_scale,
+                               float* k_min, float* k_max, void* hip_stream) {
+  bsa::Shape sh;
+  bsa_status st = check_problem(problem, sh);
+  if (st != BSA_OK) return st;
+  if (sh.S == 0) return ok();
+  if (!k || !k_min || !k_max)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "k, k_min and k_max are required");
+  if (sh.fp8 && !k_scale) return fail(BSA_ERR_INVALID_ARGUMENT, "FP8 keys need k_scale");
+  if (misaligned(k) || misaligned(k_min) || misaligned(k_max))
+    return fail(BSA_ERR_INVALID_ARGUMENT, "k, k_min and k_max must be 16-byte aligned");
+  return device_status(bsa::launch_key_bounds(sh, k, sh.fp8 ? k_scale : nullptr, k_min, k_max,
+                                              (hipStream_t)hip_stream),
+                       "bsa_pool_key_bounds launch");
+}
+
+size_t bsa_quest_scores_workspace_size(const bsa_problem* problem) {
+  bsa::Shape sh;
+  if (check_problem(problem, sh) != BSA_OK) return 0;
+  return bsa::quest_workspace_bytes(sh);
+}
+
+bsa_status bsa_quest_scores(const bsa_problem* problem, const void* q, const float* q_scale,
+                            const float* k_min, const float* k_max, float* scores,
+                            void* workspace, size_t workspace_bytes, void* hip_stream) {
+  bsa::Shape sh;
+  bsa_status st = check_problem(problem, sh);
+  if (st != BSA_OK) return st;
+  if (sh.S == 0) return ok();
+  if (!q || !k_min || !k_max || !scores)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "q, k_min, k_max and scores are required");
+  if (sh.fp8 && !q_scale) return fail(BSA_ERR_INVALID_ARGUMENT, "FP8 queries need q_scale");
+  if (misaligned(q) || misaligned(k_min) || misaligned(k_max) || misaligned(workspace))
+    return fail(BSA_ERR_INVALID_ARGUMENT, "q, k_min, k_max and workspace must be 16-byte aligned");
+  const size_t need = bsa::quest_workspace_bytes(sh);
+  if (!workspace || workspace_bytes < need)
+    return fail(BSA_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, need);
+  return device_status(bsa::launch_quest_scores(sh, q, sh.fp8 ? q_scale : nullptr, k_min, k_max,
+                                                scores, workspace, (hipStream_t)hip_stream),
+                       "bsa_quest_scores launch");
+}
+
+size_t bsa_select_scores_workspace_size(const bsa_problem* problem,
+                                        const bsa_select_params* params) {
+  bsa::Shape sh;
+  if (check_problem(problem, sh) != BSA_OK || check_params(params) != BSA_OK) return 0;
+  return bsa::select_workspace_layout(sh, true, params->gate == BSA_GATE_SIGMA_CUT).total;
+}
+
+bsa_status bsa_select_scores(const bsa_problem* problem, const bsa_select_params* params,
+                             const float* scores, int32_t* row_ptr, int32_t* col_idx,
+                             int64_t col_capacity, uint8_t* gate_out, void* workspace,
+                             size_t workspace_bytes, void* hip_stream) {
+  bsa::Shape sh;
+  bsa_status st = check_problem(problem, sh);
+  if (st != BSA_OK) return st;
+  st = check_params(params);
+  if (st != BSA_OK) return st;
+  if (params->rescue_fraction > 0.0)
+    return fail(BSA_ERR_INVALID_ARGUMENT,
+                "the rescue branch needs centroid scores and radii (use bsa_score_select)");
+  if (sh.S == 0) return ok();
+  if (!scores || !row_ptr || !col_idx)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "scores, row_ptr and col_idx are required");
+  if (misaligned(row_ptr) || misaligned(workspace))
+    return fail(BSA_ERR_INVALID_ARGUMENT, "row_ptr and workspace must be 16-byte aligned");
+  const int64_t bound = capacity_bound(sh, params);
+  if (bound > 0x7FFFFFFF)
+    return fail(BSA_ERR_UNSUPPORTED, "kept-block bound %lld exceeds int32 CSR", (long long)bound);
+  if (col_capacity < bound)
+    return fail(BSA_ERR_CAPACITY, "col_capacity %lld < bound %lld", (long long)col_capacity,
+                (long long)bound);
+  const size_t need =
+      bsa::select_workspace_layout(sh, true, params->gate == BSA_GATE_SIGMA_CUT).total;
+  if (!workspace || workspace_bytes < need)
+    return fail(BSA_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, need);
+  const bsa::SelectConfig cfg = select_config(params);
+  return device_status(
+      bsa::launch_score_select(sh, cfg, nullptr, nullptr, nullptr, nullptr, row_ptr, col_idx,
+                               col_capacity, nullptr, nullptr, gate_out, workspace,
+                               (hipStream_t)hip_stream, scores),
+      "bsa_select_scores launch");
 }
 
 bsa_status bsa_attention_fwd(const bsa_problem* problem, const void* q, const void* k,

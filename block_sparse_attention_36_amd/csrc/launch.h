@@ -34,11 +34,22 @@ struct SelectWorkspace {
 };
 SelectWorkspace select_workspace_layout(const Shape& sh, bool export_scores, bool sigma_gate);
 
+// scores_in != nullptr: selection on the given scores [U, nb, nb] (no centroid
+// scores are computed; q_centroid and k_centroid are unused).
 hipError_t launch_score_select(const Shape& sh, const SelectConfig& cfg, const float* q_centroid,
                                const float* q_norm, const float* k_centroid,
                                const float* k_radius, int32_t* row_ptr, int32_t* col_idx,
                                int64_t col_capacity, float* scores_out, float* bound_out,
-                               uint8_t* gate_out, void* workspace, hipStream_t stream);
+                               uint8_t* gate_out, void* workspace, hipStream_t stream,
+                               const float* scores_in = nullptr);
+
+hipError_t launch_key_bounds(const Shape& sh, const void* k, const float* k_scale, float* k_min,
+                             float* k_max, hipStream_t stream);
+
+size_t quest_workspace_bytes(const Shape& sh);
+hipError_t launch_quest_scores(const Shape& sh, const void* q, const float* q_scale,
+                               const float* k_min, const float* k_max, float* scores,
+                               void* workspace, hipStream_t stream);
 
 hipError_t launch_attention(const Shape& sh, const void* q, const void* k, const void* v,
                             const float* q_scale, const float* k_scale, const float* v_scale,

@@ -12,6 +12,11 @@
 // (token block, chunk of heads), rows loaded eight at a time.  Keys (far fewer
 // heads): eight waves per block split its rows, which stay in registers for the
 // radius pass.
+//
+// Key-block bounds (the Quest backbone's summary, same page, Methodology step 1:
+// per-coordinate upper bounds from K-min/K-max): the coordinate-wise minimum and
+// maximum of each block's dequantised keys, with the same row split as the key
+// centroids.
 #include "common.h"
 #include "launch.h"
 
@@ -241,6 +246,90 @@ __global__ __launch_bounds__(64 * KW) void pool_k_kernel(
   }
 }
 
+// Coordinate-wise minimum and maximum of each key block (dequantised values), one
+// workgroup of KW waves per (key block, chunk of kv heads), wave w over rows
+// [w*R, (w+1)*R); the per-wave extremes meet in LDS.
+template <bool FP8, int D, int KW, int R>
+__global__ __launch_bounds__(64 * KW) void kbounds_kernel(
+    const void* __restrict__ k, const float* __restrict__ k_scale, float* __restrict__ kmin,
+    float* __restrict__ kmax, int64_t S, int Hkv, int B, int nb, int HW) {
+  typedef RowLoad<FP8> L;
+  __shared__ f32x4 pmin[KW][64][2];
+  __shared__ f32x4 pmax[KW][64][2];
+  const int j = blockIdx.x;
+  const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int gl = (l * 8) / D, d = (l * 8) % D;
+  const int g = blockIdx.y * HW + gl;
+  const bool active = gl < HW && g < Hkv;
+  const int64_t t0 = (int64_t)j * B;
+  const int cnt = (int)((S - t0) < B ? (S - t0) : B);
+  const size_t row_bytes = (size_t)Hkv * D * L::elem_bytes;
+  const unsigned char* base = (const unsigned char*)k + (size_t)t0 * row_bytes +
+                              ((size_t)(active ? g : 0) * D + d) * L::elem_bytes;
+  const int r0 = w * R;
+  const float scale = (FP8 && active) ? k_scale[(size_t)g * nb + j] : 1.0f;
+  typename L::raw v[R];
+#pragma unroll
+  for (int u = 0; u < R; ++u)
+    if (active && r0 + u < cnt) v[u] = L::load(base + (size_t)(r0 + u) * row_bytes);
+  float lo[8], hi[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    lo[e] = INFINITY;
+    hi[e] = -INFINITY;
+  }
+#pragma unroll
+  for (int u = 0; u < R; ++u) {
+    if (active && r0 + u < cnt) {
+      float x[8];
+      L::decode(x, v[u]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float y = FP8 ? x[e] * scale : x[e];
+        lo[e] = fminf(lo[e], y);
+        hi[e] = fmaxf(hi[e], y);
+      }
+    }
+  }
+  pmin[w][l][0] = f32x4{lo[0], lo[1], lo[2], lo[3]};
+  pmin[w][l][1] = f32x4{lo[4], lo[5], lo[6], lo[7]};
+  pmax[w][l][0] = f32x4{hi[0], hi[1], hi[2], hi[3]};
+  pmax[w][l][1] = f32x4{hi[4], hi[5], hi[6], hi[7]};
+  __syncthreads();
+  if (w != 0 || !active) return;  // (no barrier follows)
+#pragma unroll
+  for (int ww = 1; ww < KW; ++ww) {
+#pragma unroll
+    for (int hq = 0; hq < 2; ++hq) {
+      const f32x4 a = pmin[ww][l][hq], b = pmax[ww][l][hq];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        lo[4 * hq + e] = fminf(lo[4 * hq + e], a[e]);
+        hi[4 * hq + e] = fmaxf(hi[4 * hq + e], b[e]);
+      }
+    }
+  }
+  const size_t o = ((size_t)g * nb + j) * D + d;
+  *(f32x4*)(kmin + o) = f32x4{lo[0], lo[1], lo[2], lo[3]};
+  *(f32x4*)(kmin + o + 4) = f32x4{lo[4], lo[5], lo[6], lo[7]};
+  *(f32x4*)(kmax + o) = f32x4{hi[0], hi[1], hi[2], hi[3]};
+  *(f32x4*)(kmax + o + 4) = f32x4{hi[4], hi[5], hi[6], hi[7]};
+}
+
+template <bool FP8, int D>
+hipError_t launch_kbounds_t(const Shape& sh, const void* k, const float* k_scale, float* kmin,
+                            float* kmax, hipStream_t stream) {
+  const int HWK = 512 / D;
+  dim3 gk(sh.nb, (sh.Hkv + HWK - 1) / HWK);
+  if (sh.B == 128)
+    hipLaunchKernelGGL((kbounds_kernel<FP8, D, 8, 16>), gk, dim3(512), 0, stream, k, k_scale,
+                       kmin, kmax, sh.S, sh.Hkv, sh.B, sh.nb, HWK);
+  else
+    hipLaunchKernelGGL((kbounds_kernel<FP8, D, 8, 8>), gk, dim3(512), 0, stream, k, k_scale,
+                       kmin, kmax, sh.S, sh.Hkv, sh.B, sh.nb, HWK);
+  return hipGetLastError();
+}
+
 template <bool FP8, int D>
 hipError_t launch_pool_t(const Shape& sh, const void* q, const void* k, const float* q_scale,
                          const float* k_scale, float* q_centroid, float* q_norm,
@@ -267,6 +356,15 @@ hipError_t launch_pool_t(const Shape& sh, const void* q, const void* k, const fl
 }
 
 }  // namespace
+
+hipError_t launch_key_bounds(const Shape& sh, const void* k, const float* k_scale, float* kmin,
+                             float* kmax, hipStream_t stream) {
+  if (sh.D == 128)
+    return sh.fp8 ? launch_kbounds_t<true, 128>(sh, k, k_scale, kmin, kmax, stream)
+                  : launch_kbounds_t<false, 128>(sh, k, k_scale, kmin, kmax, stream);
+  return sh.fp8 ? launch_kbounds_t<true, 64>(sh, k, k_scale, kmin, kmax, stream)
+                : launch_kbounds_t<false, 64>(sh, k, k_scale, kmin, kmax, stream);
+}
 
 hipError_t launch_pool(const Shape& sh, const void* q, const void* k, const float* q_scale,
                        const float* k_scale, float* q_centroid, float* q_norm, float* k_centroid,

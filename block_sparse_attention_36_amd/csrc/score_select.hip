@@ -687,26 +687,30 @@ __global__ __launch_bounds__(256) void select_reg_kernel(SelArgs a) {
 // the mean of sigma over the U units (summed in unit order).  With T tiles that
 // have a cut and r = floor(q*T) (in double), tile i fires when at most r of
 // them have a mean <= its own, i.e. when its mean lies strictly below the
-// (r+1)-th smallest, found by bisection on the order-preserving keys.  Every
-// row of a fired tile then counts its expansion blocks, and the per-tile
-// decision is left in fire[] for the compaction.
+// (r+1)-th smallest, found by bisection on the order-preserving keys.  The
+// per-tile decision is left in fire[]: a row-parallel pass adds the expansion
+// counts of fired rows before the scan, and the compaction their bits.
 constexpr unsigned kNoCut = 0xFFFFFFFFu;  // key of a tile without a cut (never a mean's key)
 
-__global__ __launch_bounds__(1024) void sigma_tile_kernel(
-    const float* __restrict__ sigma, const int* __restrict__ counts_x, int* __restrict__ counts,
-    unsigned* __restrict__ gkeys, uint8_t* __restrict__ fire, uint8_t* __restrict__ gate_out,
-    int U, int nb, int k, int sink, float q, int keys_in_lds) {
+__global__ __launch_bounds__(1024) void sigma_tile_kernel(const float* __restrict__ sigma,
+                                                          unsigned* __restrict__ gkeys,
+                                                          uint8_t* __restrict__ fire, int U,
+                                                          int nb, int k, int sink, float q,
+                                                          int keys_in_lds) {
   extern __shared__ unsigned skeys[];
-  __shared__ int part[16];
+  __shared__ int part[2][16];
   const int t = threadIdx.x, l = t & 63, w = t >> 6;
   unsigned* keys = keys_in_lds ? skeys : gkeys;
+  int parity = 0;
+  // one barrier per sum: consecutive sums alternate between the two halves of
+  // part[], and a half is rewritten only after the barrier of the sum in between
   auto block_sum = [&](int v) {
     v = wave_sum_int(v);
-    __syncthreads();  // the previous sum's readers are done with part[]
-    if (l == 0) part[w] = v;
+    if (l == 0) part[parity][w] = v;
     __syncthreads();
     int tot = 0;
-    for (int x = 0; x < 16; ++x) tot += part[x];
+    for (int x = 0; x < 16; ++x) tot += part[parity][x];
+    parity ^= 1;
     return tot;
   };
   int mine = 0;
@@ -715,13 +719,21 @@ __global__ __launch_bounds__(1024) void sigma_tile_kernel(
     unsigned key = kNoCut;
     if (nc > k) {
       float sum = 0.f;
-      for (int u = 0; u < U; ++u) sum += sigma[(size_t)u * nb + i];
+      int u = 0;
+      for (; u + 8 <= U; u += 8) {  // eight loads in flight, added in unit order
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = sigma[(size_t)(u + e) * nb + i];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sum += v[e];
+      }
+      for (; u < U; ++u) sum += sigma[(size_t)u * nb + i];
       key = float_key(sum / (float)U);
       ++mine;
     }
     keys[i] = key;
   }
-  const int T = block_sum(mine);  // (its barriers also publish keys[])
+  const int T = block_sum(mine);  // (its barrier also publishes keys[])
   const int r = (int)floor((double)q * (double)T);
   const int need = T - r;  // keys at or above the (r+1)-th smallest
   unsigned tq = 0xFFFFFFFFu;  // r >= T: every tile with a cut fires
@@ -735,13 +747,6 @@ __global__ __launch_bounds__(1024) void sigma_tile_kernel(
     }
   }
   for (int i = t; i < nb; i += 1024) fire[i] = (keys[i] != kNoCut && keys[i] < tq) ? 1 : 0;
-  const int rows = U * nb;
-  for (int row = t; row < rows; row += 1024) {
-    const unsigned key = keys[row % nb];
-    const bool f = key != kNoCut && key < tq;
-    if (f) counts[row] += counts_x[row];
-    if (gate_out) gate_out[row] = f ? 1 : 0;
-  }
 }
 
 // ------------------------------------------------------------------ CSR
@@ -801,11 +806,19 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int* __restrict__ coun
   if (t == 1023) row_ptr[rows] = clampc((int64_t)before + x);
 }
 
-// With the sigma gate, rows of fired tiles add their expansion bits (disjoint
-// from the kept bits).
+// Sigma gate: a row whose tile fired also keeps its expansion blocks.
+__global__ __launch_bounds__(256) void expand_counts_kernel(int* __restrict__ counts,
+                                                            const int* __restrict__ counts_x,
+                                                            const uint8_t* __restrict__ fire,
+                                                            int rows, int nb) {
+  const int row = blockIdx.x * 256 + threadIdx.x;
+  if (row < rows && fire[row % nb]) counts[row] += counts_x[row];
+}
+
 __global__ __launch_bounds__(256) void compact_kernel(const unsigned long long* __restrict__ mask,
                                                       const unsigned long long* __restrict__ mask_x,
                                                       const uint8_t* __restrict__ fire,
+                                                      uint8_t* __restrict__ gate_out,
                                                       const int32_t* __restrict__ row_ptr,
                                                       int32_t* __restrict__ col_idx, int rows,
                                                       int nb, int nw, int64_t capacity) {
@@ -816,6 +829,7 @@ __global__ __launch_bounds__(256) void compact_kernel(const unsigned long long* 
   const int nslots = i / 64 + 1;
   const int64_t base = row_ptr[row];
   const bool expand = fire != nullptr && fire[i];
+  if (fire != nullptr && gate_out != nullptr && l == 0) gate_out[row] = expand ? 1 : 0;
   int run = 0;
   const unsigned long long lt = lanemask_lt();
   for (int e = 0; e < nslots; ++e) {
@@ -865,20 +879,26 @@ hipError_t launch_score_select(const Shape& sh, const SelectConfig& cfg, const f
                                const float* q_norm, const float* k_centroid,
                                const float* k_radius, int32_t* row_ptr, int32_t* col_idx,
                                int64_t col_capacity, float* scores_out, float* bound_out,
-                               uint8_t* gate_out, void* workspace, hipStream_t stream) {
+                               uint8_t* gate_out, void* workspace, hipStream_t stream,
+                               const float* scores_in) {
   const bool sig = cfg.gate == 2 && cfg.top_k > 0;
-  const SelectWorkspace w = select_workspace_layout(sh, scores_out != nullptr, cfg.gate == 2);
+  const SelectWorkspace w =
+      select_workspace_layout(sh, scores_out != nullptr || scores_in != nullptr, cfg.gate == 2);
   unsigned char* ws = (unsigned char*)workspace;
-  float* scores = scores_out ? scores_out : (float*)(ws + w.scores_off);
+  float* scores = scores_in ? const_cast<float*>(scores_in)  // read only below
+                            : scores_out ? scores_out : (float*)(ws + w.scores_off);
   unsigned long long* mask = (unsigned long long*)(ws + w.mask_off);
   int* counts = (int*)(ws + w.counts_off);
   const int nb = sh.nb, U = sh.U(), rows = U * nb, nw = (nb + 63) / 64;
   const int NT = (nb + 63) / 64;
 
-  hipLaunchKernelGGL(score_kernel, dim3(NT, NT, U), dim3(256), 0, stream, q_centroid, k_centroid,
-                     scores, nb, sh.D, sh.G(), sh.per_group);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
+  if (!scores_in) {
+    hipLaunchKernelGGL(score_kernel, dim3(NT, NT, U), dim3(256), 0, stream, q_centroid,
+                       k_centroid, scores, nb, sh.D, sh.G(), sh.per_group);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
 
   SelArgs a;
   a.scores = scores;
@@ -946,18 +966,24 @@ hipError_t launch_score_select(const Shape& sh, const SelectConfig& cfg, const f
     fire = ws + w.fire_off;
     const int in_lds = nb <= 8192 ? 1 : 0;  // 32 KiB of keys
     hipLaunchKernelGGL(sigma_tile_kernel, dim3(1), dim3(1024), in_lds ? nb * sizeof(unsigned) : 0,
-                       stream, a.sigma, a.counts_x, counts, (unsigned*)(ws + w.keys_off), fire,
-                       gate_out, U, nb, cfg.top_k, cfg.force_sink, cfg.gate_threshold, in_lds);
+                       stream, a.sigma, (unsigned*)(ws + w.keys_off), fire, U, nb, cfg.top_k,
+                       cfg.force_sink, cfg.gate_threshold, in_lds);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }  // (with the top-k branch off the select kernel writes gate_out = 0 itself)
 
+  if (fire) {
+    hipLaunchKernelGGL(expand_counts_kernel, dim3((rows + 255) / 256), dim3(256), 0, stream,
+                       counts, a.counts_x, fire, rows, nb);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, stream, counts, row_ptr, rows,
                      col_capacity);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(compact_kernel, dim3((rows + 3) / 4), dim3(256), 0, stream, mask, a.mask_x,
-                     fire, row_ptr, col_idx, rows, nb, nw, col_capacity);
+                     fire, gate_out, row_ptr, col_idx, rows, nb, nw, col_capacity);
   return hipGetLastError();
 }
 

@@ -12,6 +12,13 @@
  *   bsa_attention_fwd  online-softmax attention of every query block over its kept
  *                      key blocks only, with the causal mask on the diagonal block.
  *
+ * The Quest backbone replaces the first two calls by three:
+ *
+ *   bsa_pool_key_bounds  coordinate-wise minimum and maximum of every key block;
+ *   bsa_quest_scores     per query row the largest q.k over each block's box, and
+ *                        per query tile the maximum over its rows;
+ *   bsa_select_scores    the selection rules of bsa_score_select on given scores.
+ *
  * Sources (the method these calls compute):
  *   - "Uncertainty-gated selection for block-sparse attention" (gist.science),
  *     technical summary, Methodology steps 1-2 (block scores from mean-pooled
@@ -60,7 +67,7 @@
 extern "C" {
 #endif
 
-#define BSA_ABI_VERSION 1
+#define BSA_ABI_VERSION 2
 
 typedef enum {
   BSA_OK = 0,
@@ -183,6 +190,63 @@ bsa_status bsa_score_select(const bsa_problem* problem, const bsa_select_params*
                             int32_t* col_idx, int64_t col_capacity, float* scores_out,
                             float* bound_out, uint8_t* gate_out, void* workspace,
                             size_t workspace_bytes, void* hip_stream);
+
+/*
+ * bsa_pool_key_bounds -- the Quest backbone's key-block summary ("Uncertainty-gated
+ * selection ...", Methodology step 1: per-coordinate upper bounds from K-min/K-max).
+ *
+ *   k            [S, Hkv, D] bf16, or E4M3 codes with k_scale [Hkv, nb].
+ *   k_min, k_max out [Hkv, nb, D] f32: the coordinate-wise minimum / maximum over
+ *                the block's keys (dequantised values; a ragged last block over
+ *                the rows it has).
+ */
+bsa_status bsa_pool_key_bounds(const bsa_problem* problem, const void* k, const float* k_scale,
+                               float* k_min, float* k_max, void* hip_stream);
+
+/* Device workspace bytes bsa_quest_scores needs (0 on an invalid problem). */
+size_t bsa_quest_scores_workspace_size(const bsa_problem* problem);
+
+/*
+ * bsa_quest_scores -- Quest tile scores (same page, Methodology steps 1-2: the
+ * per-coordinate upper bound as the block score of a query row; a tile's score is
+ * the maximum over its rows).
+ *
+ *   scores[u][i][j] = max over the query rows t of block i, and over the heads of
+ *   unit u, of  sum_d max(q[t][h][d] * k_min[g][j][d], q[t][h][d] * k_max[g][j][d])
+ *   for j <= i (g the unit's kv head; other entries untouched).  For E4M3 queries
+ *   q is code * q_scale[h][i]; q_scale must be >= 0.
+ *
+ *   q            [S, Hq, D] bf16, or E4M3 codes with q_scale [Hq, nb].
+ *   k_min, k_max as bsa_pool_key_bounds writes them.
+ *   scores       out f32 [U, nb, nb].
+ *   workspace    at least bsa_quest_scores_workspace_size() bytes, else
+ *                BSA_ERR_WORKSPACE (bounds repacked for the matrix cores).
+ * The bound is computed on the bf16 matrix cores with fp32 accumulation: exact
+ * products for bf16 inputs; bounds of E4M3 keys enter as a bf16 head plus tail
+ * (relative representation error <= 2^-18).
+ */
+bsa_status bsa_quest_scores(const bsa_problem* problem, const void* q, const float* q_scale,
+                            const float* k_min, const float* k_max, float* scores,
+                            void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* Device workspace bytes bsa_select_scores needs (0 on invalid arguments). */
+size_t bsa_select_scores_workspace_size(const bsa_problem* problem,
+                                        const bsa_select_params* params);
+
+/*
+ * bsa_select_scores -- bsa_score_select's selection rules (top-k, both gates, the
+ * mass branch, forced blocks, CSR) on caller-provided scores [U, nb, nb] (entries
+ * j <= i read), e.g. from bsa_quest_scores ("Uncertainty-gated selection ...",
+ * technical summary: the router sits on top of any scoring backbone).  The
+ * rescue branch is defined on centroid scores and radii, so rescue_fraction must
+ * be 0 (BSA_ERR_INVALID_ARGUMENT otherwise).  row_ptr, col_idx, col_capacity,
+ * gate_out as in bsa_score_select; workspace of at least
+ * bsa_select_scores_workspace_size() bytes.
+ */
+bsa_status bsa_select_scores(const bsa_problem* problem, const bsa_select_params* params,
+                             const float* scores, int32_t* row_ptr, int32_t* col_idx,
+                             int64_t col_capacity, uint8_t* gate_out, void* workspace,
+                             size_t workspace_bytes, void* hip_stream);
 
 /*
  * bsa_attention_fwd -- attention over the kept blocks (RBS-Attention, third

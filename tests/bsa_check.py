@@ -61,6 +61,8 @@ class GpuRun:
     scores: torch.Tensor
     bounds: torch.Tensor | None
     gate: np.ndarray
+    kmin: torch.Tensor | None = None  # Quest backbone: key-block bounds
+    kmax: torch.Tensor | None = None
 
 
 def run_gpu(cfg, inp) -> GpuRun:
@@ -68,6 +70,18 @@ def run_gpu(cfg, inp) -> GpuRun:
     q, k, v = inp.q, inp.k, inp.v
     problem = bsa.make_problem(q, k, cfg.block_size, granularity_code(cfg))
     params = lib_params(cfg)
+    if cfg.backbone == "quest":
+        kmin, kmax = bsa.bsa_pool_key_bounds(problem, k, inp.k_scale)
+        scores = bsa.bsa_quest_scores(problem, q, kmin, kmax, inp.q_scale)
+        sel = bsa.bsa_select_scores(problem, params, scores, export=True)
+        out, lse = bsa.bsa_attention_fwd(problem, q, k, v, sel.row_ptr, sel.col_idx,
+                                         1.0 / math.sqrt(cfg.head_dim), inp.q_scale, inp.k_scale,
+                                         inp.v_scale)
+        torch.cuda.synchronize()
+        rp = sel.row_ptr.cpu().numpy().astype(np.int64)
+        ci = sel.col_idx[: int(rp[-1])].cpu().numpy().astype(np.int64)
+        return GpuRun(out, lse, rp, ci, None, None, None, None, scores, None,
+                      sel.gate.cpu().numpy(), kmin, kmax)
     pool = bsa.bsa_pool(problem, q, k, inp.q_scale, inp.k_scale)
     sel = bsa.bsa_score_select(problem, params, pool, export=True)
     out, lse = bsa.bsa_attention_fwd(problem, q, k, v, sel.row_ptr, sel.col_idx,
@@ -158,19 +172,63 @@ def check_all(cfg, inp_gpu, run: GpuRun, row_sample=None, unit_sample=None,
     """Compare pool, scores/bounds, masks and outputs.  Samples: None = everything."""
     rep = Report()
     rng = np.random.default_rng(rng_seed)
-    B, S, D = cfg.block_size, cfg.seq_len, cfg.head_dim
-    Hq, Hkv, G, nb, U = cfg.num_q_heads, cfg.num_kv_heads, cfg.group_size, cfg.num_blocks, cfg.num_units
-    gran = cfg.granularity
+    nb = cfg.num_blocks
     host = HostInputs(cfg, inp_gpu)
-    p = params_of(cfg)
+    blocks = list(range(nb)) if row_sample is None else sorted(set(
+        [0, nb - 1] + list(rng.choice(nb, size=min(nb, 24), replace=False))))
+    if cfg.backbone == "quest":
+        _check_quest_pool_and_scores(cfg, host, run, blocks, rng, score_sample)
+    else:
+        _check_pool_and_scores(cfg, host, run, blocks, rng, score_sample)
+    _check_masks_and_outputs(cfg, host, run, rep, params_of(cfg), rng, row_sample, unit_sample)
+    return rep
+
+
+def _check_quest_pool_and_scores(cfg, host, run, blocks, rng, score_sample):
+    """Key-block bounds bit-exact (after rounding the oracle's value to float32) and
+    Quest tile scores within 1e-4 * max_t ||q_t|| * ||max(|k_min|, |k_max|)||."""
+    B, nb, U = cfg.block_size, cfg.num_blocks, cfg.num_units
+    Hq, Hkv, gran = cfg.num_q_heads, cfg.num_kv_heads, cfg.granularity
+    G = cfg.group_size
+    kmin = run.kmin.cpu().numpy()
+    kmax = run.kmax.cpu().numpy()
+    for j in blocks:
+        rmin, rmax = O.key_block_bounds(host.rows("k", [j]), B)
+        assert np.array_equal(kmin[:, j], rmin[:, 0].astype(np.float32)), f"k_min block {j}"
+        assert np.array_equal(kmax[:, j], rmax[:, 0].astype(np.float32)), f"k_max block {j}"
+    if score_sample is None:
+        ent = [(u, i, j) for u in range(U) for i in range(nb) for j in range(i + 1)]
+    else:
+        ent = [(int(rng.integers(U)), i, 0) for i in rng.integers(nb, size=score_sample)]
+        ent = [(u, i, int(rng.integers(i + 1))) for (u, i, _) in ent]
+        ent += [(0, nb - 1, nb - 1), (U - 1, nb - 1, 0)]
+    by_block = {}
+    for (u, i, j) in ent:
+        by_block.setdefault(i, []).append((u, j))
+    s_gpu = run.scores
+    for i, lst in by_block.items():
+        Qi = host.rows("q", [i])
+        for (u, j) in lst:
+            heads = [u] if gran == "qhead" else list(range(u * G, (u + 1) * G))
+            g = O.kv_of_unit(u, Hq, Hkv, gran)
+            rmin, rmax = O.key_block_bounds(host.rows("k", [j])[:, g:g + 1, :], B)
+            rows = Qi[:, heads, :].reshape(-1, cfg.head_dim)
+            sref = float(O.quest_row_bound(rows, rmin[0, :1], rmax[0, :1]).max())
+            kabs = np.maximum(np.abs(rmin[0, 0]), np.abs(rmax[0, 0]))
+            tol = 1e-4 * np.linalg.norm(rows, axis=1).max() * np.linalg.norm(kabs)
+            sg = float(s_gpu[u, i, j])
+            assert abs(sg - sref) <= tol + 1e-30, f"quest score ({u},{i},{j}): {sg} vs {sref}"
+
+
+def _check_pool_and_scores(cfg, host, run, blocks, rng, score_sample):
+    B, nb, U = cfg.block_size, cfg.num_blocks, cfg.num_units
+    Hq, Hkv, gran = cfg.num_q_heads, cfg.num_kv_heads, cfg.granularity
     qc = run.qc.cpu().numpy().astype(np.float64)
     kc = run.kc.cpu().numpy().astype(np.float64)
     qn = run.qn.cpu().numpy().astype(np.float64)
     kr = run.kr.cpu().numpy().astype(np.float64)
 
     # ---- pool: sampled (or all) blocks
-    blocks = list(range(nb)) if row_sample is None else sorted(set(
-        [0, nb - 1] + list(rng.choice(nb, size=min(nb, 24), replace=False))))
     for i in blocks:
         Qi = host.rows("q", [i])
         Ki = host.rows("k", [i])
@@ -210,6 +268,15 @@ def check_all(cfg, inp_gpu, run: GpuRun, row_sample=None, unit_sample=None,
                 bref = sref + qnorm[u, 0] * rad[0, 0]
                 bb = 1e-4 * np.linalg.norm(qbar[u, 0]) * (np.linalg.norm(kbar[0, 0]) + rad[0, 0])
                 assert abs(float(b_gpu[u, i, j]) - bref) <= bb + 1e-30, f"bound ({u},{i},{j})"
+
+
+def _check_masks_and_outputs(cfg, host, run, rep, p, rng, row_sample, unit_sample):
+    B, S, D = cfg.block_size, cfg.seq_len, cfg.head_dim
+    Hq, Hkv, G, nb, U = cfg.num_q_heads, cfg.num_kv_heads, cfg.group_size, cfg.num_blocks, cfg.num_units
+    gran = cfg.granularity
+    s_gpu = run.scores
+    b_gpu = run.bounds
+    units = list(range(U))
 
     # ---- sigma gate: the per-tile decision over the whole layer, from the exported
     # scores (every row's sigma is needed, whatever the row sample)
@@ -287,4 +354,3 @@ def check_all(cfg, inp_gpu, run: GpuRun, row_sample=None, unit_sample=None,
     assert rep.max_abs <= mx, f"output max-abs {rep.max_abs} > {mx}"
     assert rep.mean_abs <= mn, f"output mean-abs {rep.mean_abs} > {mn}"
     assert rep.lse_max <= 1e-3, f"lse max-abs {rep.lse_max}"
-    return rep

@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.bsa_abi_version() == 1
+    assert lib.bsa_abi_version() == 2
     assert lib.bsa_status_string(0) == b"ok"
     assert lib.bsa_status_string(3) == b"CSR capacity too small"
 
@@ -152,6 +152,36 @@ def test_sigma_gate_bound_and_workspace(lib):
     w0 = lib.bsa_score_select_workspace_size(ctypes.byref(p), ctypes.byref(s0), 0)
     w2 = lib.bsa_score_select_workspace_size(ctypes.byref(p), ctypes.byref(s), 0)
     assert w2 >= w0 + U * nb * (4 + 8 + 4) + nb * 5
+
+
+def test_quest_entry_points_validate_before_launching(lib):
+    p = _prob()
+    # key bounds: k, k_min and k_max are required; FP8 keys need their scales
+    assert lib.bsa_pool_key_bounds(ctypes.byref(p), FAKE, None, None, FAKE, None) == 1
+    p8 = _prob(dtype=bsa.BSA_FP8_E4M3)
+    assert lib.bsa_pool_key_bounds(ctypes.byref(p8), FAKE, None, FAKE, FAKE, None) == 1
+    # Quest scores: workspace size covers the repacked bounds, checked before launch
+    ws = lib.bsa_quest_scores_workspace_size(ctypes.byref(p))
+    nb = lib.bsa_num_blocks(ctypes.byref(p))
+    assert ws >= p.num_kv_heads * nb * 2 * p.head_dim * 2
+    assert lib.bsa_quest_scores_workspace_size(ctypes.byref(p8)) >= 2 * ws - 256
+    assert lib.bsa_quest_scores(ctypes.byref(p), FAKE, None, FAKE, FAKE, FAKE, FAKE, ws - 1,
+                                None) == 4
+    assert lib.bsa_quest_scores(ctypes.byref(p8), FAKE, None, FAKE, FAKE, FAKE, FAKE, 10**12,
+                                None) == 1
+    # selection on given scores: no rescue branch, capacity and workspace checked
+    s = bsa.make_params(top_k=4, force_sink=1, gate=bsa.BSA_GATE_SIGMA_CUT, gate_threshold=0.3)
+    cap = lib.bsa_csr_capacity_bound(ctypes.byref(p), ctypes.byref(s))
+    wss = lib.bsa_select_scores_workspace_size(ctypes.byref(p), ctypes.byref(s))
+    assert wss < lib.bsa_score_select_workspace_size(ctypes.byref(p), ctypes.byref(s), 0)
+    assert lib.bsa_select_scores(ctypes.byref(p), ctypes.byref(s), FAKE, FAKE, FAKE, cap - 1,
+                                 None, FAKE, wss, None) == 3
+    assert lib.bsa_select_scores(ctypes.byref(p), ctypes.byref(s), FAKE, FAKE, FAKE, cap, None,
+                                 FAKE, wss - 1, None) == 4
+    sr = bsa.make_params(top_k=4, rescue_fraction=0.05)
+    assert lib.bsa_select_scores(ctypes.byref(p), ctypes.byref(sr), FAKE, FAKE, FAKE, 10**9,
+                                 None, FAKE, 10**12, None) == 1
+    assert b"rescue" in lib.bsa_last_error()
 
 
 def test_attention_rejects_bad_arguments(lib):

@@ -92,6 +92,29 @@ def test_extra_workloads(cfg):
         torch.cuda.empty_cache()
 
 
+# the Quest backbone over every (head_dim, block_size) pair and input format, plus
+# per-group units (the maximum over a group's heads), ragged tails
+QUEST = [scaled(config_by_name("quest64k"), 2048 + tail, num_q_heads=8, num_kv_heads=2,
+                head_dim=d, block_size=b, dtype=dt, top_k=8, granularity=gran,
+                name=f"quest-{dt}-{gran}-D{d}-B{b}")
+         for (dt, gran, tail) in (("bf16", "qhead", 37), ("fp8", "qhead", 70),
+                                  ("bf16", "group", 5))
+         for d, b in ((64, 64), (64, 128), (128, 64), (128, 128))]
+
+
+@pytest.mark.parametrize("cfg", QUEST, ids=[c.name for c in QUEST])
+def test_quest_backbone_parity(cfg):
+    _gpu_or_skip()
+    import bsa_check as K
+    print(f"[parity-quest] {cfg.name} S={cfg.seq_len}", flush=True)
+    inp = generate(cfg, "cpu").to("cuda")
+    run = K.run_gpu(cfg, inp)
+    rep = K.check_all(cfg, inp, run)
+    print(f"  rows={rep.rows_checked} ambiguous={rep.ambiguous_rows} tiles_fired="
+          f"{rep.gate_fired_tiles} max_abs={rep.max_abs:.3g} lse={rep.lse_max:.3g}", flush=True)
+    assert rep.ambiguous_rows <= max(1, rep.rows_checked // 100)
+
+
 MID = [scaled(config_by_name("msa1m"), 2000 * 128 + 17, num_q_heads=4, num_kv_heads=2),
        scaled(config_by_name("dual128k"), 4000 * 128 - 3, num_q_heads=2, num_kv_heads=1),
        scaled(config_by_name("gated64k"), 3000 * 128, num_q_heads=2, num_kv_heads=1),

@@ -20,7 +20,11 @@ def _oracle_run(cfg, inp):
                                cfg.block_size)
     qbar, qn = O.pool_queries(Q, cfg.block_size, cfg.num_kv_heads, cfg.granularity)
     kbar, kr = O.pool_keys(Kk, cfg.block_size)
-    s = O.block_scores(qbar, kbar, cfg.num_q_heads, cfg.num_kv_heads, cfg.granularity)
+    kmin, kmax = O.key_block_bounds(Kk, cfg.block_size)
+    if cfg.backbone == "quest":
+        s = O.quest_scores(Q, kmin, kmax, cfg.block_size, cfg.num_kv_heads, cfg.granularity)
+    else:
+        s = O.block_scores(qbar, kbar, cfg.num_q_heads, cfg.num_kv_heads, cfg.granularity)
     s32 = np.nan_to_num(s).astype(np.float32)
     p = K.params_of(cfg)
     kept, fired = O.select(s32.astype(np.float64), None, p)
@@ -30,7 +34,7 @@ def _oracle_run(cfg, inp):
     f32 = lambda a: torch.from_numpy(np.asarray(a, dtype=np.float32))  # noqa: E731
     return K.GpuRun(torch.from_numpy(out).to(torch.bfloat16), f32(lse), rp, ci, f32(qbar),
                     f32(qn), f32(kbar), f32(kr), torch.from_numpy(s32), None,
-                    fired.reshape(-1).astype(np.uint8))
+                    fired.reshape(-1).astype(np.uint8), f32(kmin), f32(kmax))
 
 
 @pytest.fixture(scope="module")
@@ -76,3 +80,21 @@ def test_boundary_band_marks_only_near_ties():
     # a boundary with room on both sides leaves nothing in doubt, the boundary tile included
     assert not K.sigma_boundary_band(np.array([0.1, 0.2, 0.3, 0.5]), 0.5, 1e-5).any()
     assert not K.sigma_boundary_band(np.array([0.1, 0.2, 0.3, 0.5]), 0.2, 1e-5).any()
+
+
+@pytest.mark.parametrize("gran", ["qhead", "group"])
+def test_harness_accepts_oracle_quest_results_and_rejects_a_wrong_bound(gran):
+    cfg = scaled(config_by_name("quest64k"), 64 * 40 + 9, num_q_heads=4, num_kv_heads=2,
+                 block_size=64, head_dim=64, top_k=5, granularity=gran, name=f"quest-cpu-{gran}")
+    inp = generate(cfg, "cpu")
+    run = _oracle_run(cfg, inp)
+    rep = K.check_all(cfg, inp, run)
+    assert rep.rows_checked == cfg.num_units * cfg.num_blocks and rep.max_abs < 1e-2
+    bad = run.kmax.clone()
+    bad[0, 3, 5] += 1e-3
+    with pytest.raises(AssertionError, match="k_max block 3"):
+        K.check_all(cfg, inp, K.GpuRun(**{**run.__dict__, "kmax": bad}))
+    sc = run.scores.clone()
+    sc[0, 7, 2] *= 1.01
+    with pytest.raises(AssertionError, match="quest score"):
+        K.check_all(cfg, inp, K.GpuRun(**{**run.__dict__, "scores": sc}))

@@ -47,6 +47,7 @@ class WorkloadConfig:
     score_temperature: float = 1.0
     mass_threshold: float = 0.0  # 0 = base mass branch off
     rescue_fraction: float = 0.0  # 0 = rescue branch off
+    backbone: str = "mean_pool"  # "mean_pool" (pooled-query centroid scores) or "quest"
     # planted structure
     structure: str = "needles"  # "needles", "pairs", "mixture"
     low_rank: int = 0
@@ -117,9 +118,15 @@ CONFIGS = [
 # distribution ("Uncertainty-gated selection for block-sparse attention",
 # technical summary, Methodology steps 3-5; q matches the fraction of query
 # blocks the generator plants near-ties in).  Same seeds and inputs as gated64k.
+#
+# The same router on the Quest backbone, the pairing behind the page's LongBench-v2
+# result: K-min/K-max per key block, per-row upper bounds, a tile's score the
+# maximum over its rows (same page, Methodology steps 1-2 and Results).
 EXTRA_CONFIGS = [
     dataclasses.replace(CONFIGS[3], name="dual128k_fp8", dtype="fp8"),
     dataclasses.replace(CONFIGS[2], name="sigma64k", gate="sigma_cut", gate_threshold=0.30),
+    dataclasses.replace(CONFIGS[2], name="quest64k", gate="sigma_cut", gate_threshold=0.30,
+                        backbone="quest"),
 ]
 
 
