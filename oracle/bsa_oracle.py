@@ -63,7 +63,8 @@ __all__ = [
     "pool_queries", "pool_keys", "block_scores", "rescue_bounds", "candidate_sets",
     "descending_order", "top_k", "gate_gap", "sigma_cut_margin", "sigma_gate_tiles",
     "sigma_matrix", "tile_gate", "key_block_bounds", "quest_row_bound", "quest_scores", "mass_prefix_length", "rescue_count",
-    "select_row", "acceptable_row_sets", "select", "to_csr", "from_csr",
+    "select_row", "acceptable_row_sets", "select", "to_csr", "from_csr", "padded_width",
+    "to_padded",
     "attend", "block_tokens", "attention_unit", "attention", "dense_causal_attention", "block_of", "unit_of_head",
     "kv_of_unit",
 ]
@@ -514,6 +515,38 @@ def to_csr(kept):
         row_ptr[n + 1] = row_ptr[n] + len(r)
     col_idx = np.array([j for r in rows for j in r], dtype=np.int64)
     return row_ptr, col_idx
+
+
+def padded_width(nb: int, p: SelectParams) -> int:
+    """Slots per row of the sentinel-padded index list: the largest kept set the
+    rule can produce in any row, so one uniform shape holds every row whether
+    or not its gate fired ("Uncertainty-gated selection ...", technical summary,
+    Methodology step 5: non-triggered tiles padded with sentinels).  A row keeps
+    its forced blocks plus at most rho*k (gated) or k by top-k, at most
+    ceil(phi*|C|) by rescue, and every candidate when the mass branch is on."""
+    width = 0
+    for i in range(nb):
+        forced, cands = candidate_sets(i, p.force_sink)
+        n = len(forced)
+        if p.mass_threshold > 0.0:
+            n += len(cands)
+        else:
+            if p.top_k > 0:
+                n += min(len(cands), p.top_k * (p.gate_factor if p.gate != "none" else 1))
+            if p.rescue_fraction > 0.0:
+                n += rescue_count(len(cands), p.rescue_fraction)
+        width = max(width, min(n, i + 1))
+    return width
+
+
+def to_padded(kept, width: int) -> np.ndarray:
+    """[rows, width] block ids: each row's kept blocks ascending, then -1."""
+    rows = [r for unit in kept for r in unit]
+    out = np.full((len(rows), width), -1, dtype=np.int64)
+    for n, r in enumerate(rows):
+        assert len(r) <= width
+        out[n, : len(r)] = r
+    return out
 
 
 def from_csr(row_ptr, col_idx, U: int, nb: int):

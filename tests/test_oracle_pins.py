@@ -517,6 +517,41 @@ def test_union_and_forced_identities():
         assert all(0 <= j <= i for j in kept)
 
 
+def test_padded_width_fits_every_row_and_is_attained():
+    # brute force over random layers: every kept set fits, and with top-k (gated or
+    # not) some row fills the width exactly
+    rng = np.random.default_rng(60)
+    for p in (O.SelectParams(top_k=3, force_sink=True),
+              O.SelectParams(top_k=3, force_sink=True, gate="top12_gap", gate_threshold=1.0),
+              O.SelectParams(top_k=3, force_sink=False, gate="sigma_cut", gate_threshold=1.0),
+              O.SelectParams(top_k=2, rescue_fraction=0.25),
+              O.SelectParams(mass_threshold=0.9)):
+        nb = 14
+        s = rng.normal(0, 3, size=(2, nb, nb))
+        b = s + rng.uniform(0, 2, size=s.shape)
+        kept, _ = O.select(s, b, p.as_library_precision())
+        w = O.padded_width(nb, p)
+        lens = [len(r) for unit in kept for r in unit]
+        assert max(lens) <= w
+        if p.mass_threshold == 0.0 and p.rescue_fraction == 0.0 and p.gate != "top12_gap":
+            assert max(lens) == w  # (branches of a union may overlap, so only top-k attains)
+    # closed forms: top-k + sink + diagonal, gated to rho*k: rho*k + 2 once rows are long
+    assert O.padded_width(100, O.SelectParams(top_k=32, force_sink=True, gate="sigma_cut")) == 66
+    assert O.padded_width(100, O.SelectParams(top_k=32, force_sink=True)) == 34
+    assert O.padded_width(10, O.SelectParams(top_k=32, force_sink=True)) == 10  # whole rows
+    assert O.padded_width(7, O.SelectParams(mass_threshold=0.9)) == 7
+
+
+def test_padded_rows_hold_the_kept_sets_then_sentinels():
+    kept = [[[0], [0, 1], [1, 2]], [[0], [1], [0, 2]]]
+    pad = O.to_padded(kept, 3)
+    assert pad.tolist() == [[0, -1, -1], [0, 1, -1], [1, 2, -1], [0, -1, -1], [1, -1, -1],
+                            [0, 2, -1]]
+    rp, ci = O.to_csr(kept)
+    for r in range(6):
+        assert [x for x in pad[r] if x >= 0] == list(ci[rp[r]:rp[r + 1]])
+
+
 def test_csr_round_trip():
     kept = [[[0], [0, 1], [0, 2]], [[0], [1], [1, 2]]]
     rp, ci = O.to_csr(kept)
