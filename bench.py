@@ -287,6 +287,8 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="dual128k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--index-format", choices=("csr", "padded"), default="csr",
+                    help="kept-block lists as CSR, or as the uniform sentinel-padded list")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run one plain device copy of 1 GiB (counter calibration)")
@@ -332,7 +334,11 @@ def main(argv=None) -> int:
     else:
         pool = bsa.bsa_pool(problem, inp.q, inp.k, inp.q_scale, inp.k_scale, want_norm=rescue,
                             want_radius=rescue)
-    bufs = bsa.SelectBuffers(problem, params, dev, export=False, given_scores=quest)
+    padded = args.index_format == "padded"
+    if padded:
+        pbufs = bsa.PaddedBuffers(problem, params, dev, export=False, given_scores=quest)
+    else:
+        bufs = bsa.SelectBuffers(problem, params, dev, export=False, given_scores=quest)
     out = torch.empty(cfg.seq_len, cfg.num_q_heads, cfg.head_dim, dtype=torch.bfloat16, device=dev)
     lse = torch.empty(cfg.num_q_heads, cfg.seq_len, dtype=torch.float32, device=dev)
     scale = 1.0 / math.sqrt(cfg.head_dim)
@@ -346,17 +352,26 @@ def main(argv=None) -> int:
             bsa.bsa_pool(problem, inp.q, inp.k, inp.q_scale, inp.k_scale, out=pool)
         if ev:
             ev[1].record()
+        sc = None
         if quest:
             sc = bsa.bsa_quest_scores(problem, inp.q, kb[0], kb[1], inp.q_scale, buffers=qbufs)
             if ev:
                 ev[4].record()
+        if padded:
+            bsa.bsa_score_select_padded(problem, params, pool=None if quest else pool, scores=sc,
+                                        buffers=pbufs)
+        elif quest:
             sel = bsa.bsa_select_scores(problem, params, sc, buffers=bufs)
         else:
             sel = bsa.bsa_score_select(problem, params, pool, buffers=bufs)
         if ev:
             ev[2].record()
-        bsa.bsa_attention_fwd(problem, inp.q, inp.k, inp.v, sel.row_ptr, sel.col_idx, scale,
-                              inp.q_scale, inp.k_scale, inp.v_scale, out=out, lse=lse)
+        if padded:
+            bsa.bsa_attention_fwd_padded(problem, inp.q, inp.k, inp.v, pbufs.kv_idx, scale,
+                                         inp.q_scale, inp.k_scale, inp.v_scale, out=out, lse=lse)
+        else:
+            bsa.bsa_attention_fwd(problem, inp.q, inp.k, inp.v, sel.row_ptr, sel.col_idx, scale,
+                                  inp.q_scale, inp.k_scale, inp.v_scale, out=out, lse=lse)
         if ev:
             ev[3].record()
 
@@ -373,9 +388,15 @@ def main(argv=None) -> int:
         step(evs[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    rp = bufs.row_ptr.cpu().numpy()  # the CSR of the timed steps (deterministic)
+    if padded:  # the kept lists of the timed steps (deterministic), as CSR for counting
+        pad = pbufs.kv_idx.cpu().numpy()
+        counts = (pad >= 0).sum(axis=1)
+        rp = np.concatenate([[0], np.cumsum(counts)])
+        ci = pad[pad >= 0]
+    else:
+        rp = bufs.row_ptr.cpu().numpy()  # the CSR of the timed steps (deterministic)
+        ci = bufs.col_idx[:int(rp[-1])].cpu().numpy()
     nnz = int(rp[-1])
-    ci = bufs.col_idx[:nnz].cpu().numpy()
     kept_flops = attention_flops(rp, ci, cfg)
     pool_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     sel_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
@@ -421,6 +442,7 @@ def main(argv=None) -> int:
         "density": round(nnz / causal_blocks, 5),
         "dense_causal_tflop": round(dense / 1e12, 3),
         "backbone": cfg.backbone,
+        "index_format": args.index_format,
         "pool_select": {"algorithmic_gb": round(ps_bytes / 1e9, 4),
                         "gbs": round(ps_bytes / (ps_ms * 1e-3) / 1e9, 1),
                         "frac_hbm": round(ps_bytes / (ps_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},

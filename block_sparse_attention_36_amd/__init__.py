@@ -86,6 +86,11 @@ def load_library(path: str = LIB_PATH):
         "bsa_quest_scores": ([PP, P, P, P, P, P, P, SZ, P], ctypes.c_int),
         "bsa_select_scores_workspace_size": ([PP, PS], SZ),
         "bsa_select_scores": ([PP, PS, P, P, P, I64, P, P, SZ, P], ctypes.c_int),
+        "bsa_padded_width": ([PP, PS], I64),
+        "bsa_score_select_padded_workspace_size": ([PP, PS, ctypes.c_int], SZ),
+        "bsa_score_select_padded": ([PP, PS, P, P, P, P, P, P, I64, P, P, P, P, SZ, P],
+                                    ctypes.c_int),
+        "bsa_attention_fwd_padded": ([PP, P, P, P, P, P, P, P, I64, F, P, P, P], ctypes.c_int),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(L, name)
@@ -275,6 +280,71 @@ def bsa_select_scores(problem: Problem, params: SelectParams, scores, export=Fal
                                _ptr(b.row_ptr), _ptr(b.col_idx), b.capacity, _ptr(b.gate),
                                _ptr(b.workspace), b.workspace.numel(), _stream(dev)))
     return Selection(b.row_ptr, b.col_idx, None, scores if export else None, None, b.gate)
+
+
+class PaddedBuffers:
+    """The padded list [U*nb, width] and the workspace of bsa_score_select_padded."""
+
+    def __init__(self, problem: Problem, params: SelectParams, device, export=False,
+                 given_scores=False):
+        import torch
+        L = load_library()
+        rows = L.bsa_num_select_rows(ctypes.byref(problem))
+        width = L.bsa_padded_width(ctypes.byref(problem), ctypes.byref(params))
+        if rows < 0 or width < 0:
+            _check(L.bsa_score_select_padded(ctypes.byref(problem), ctypes.byref(params), None,
+                                             None, None, None, None, None, 0, None, None, None,
+                                             None, 0, None))
+        nb = L.bsa_num_blocks(ctypes.byref(problem))
+        U = rows // max(nb, 1)
+        ws = L.bsa_score_select_padded_workspace_size(ctypes.byref(problem), ctypes.byref(params),
+                                                      int(export or given_scores))
+        self.width = max(int(width), 1)
+        self.kv_idx = torch.empty(rows, self.width, dtype=torch.int32, device=device)
+        self.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=device)
+        self.scores = self.bounds = self.gate = None
+        if export:
+            if not given_scores:
+                self.scores = torch.empty(U, nb, nb, dtype=torch.float32, device=device)
+                if params.rescue_fraction > 0:
+                    self.bounds = torch.empty(U, nb, nb, dtype=torch.float32, device=device)
+            self.gate = torch.empty(rows, dtype=torch.uint8, device=device)
+
+
+def bsa_score_select_padded(problem: Problem, params: SelectParams, pool: PoolResult | None = None,
+                            scores=None, export=False, buffers: PaddedBuffers | None = None):
+    """Selection as a padded list (centroid scores from pool, or the given scores).
+    Returns the buffers (kv_idx, width, and with export the scores/bounds/gate)."""
+    L = load_library()
+    dev = (scores if scores is not None else pool.q_centroid).device
+    b = buffers or PaddedBuffers(problem, params, dev, export, given_scores=scores is not None)
+    pc = (None, None, None, None) if pool is None else (pool.q_centroid, pool.q_norm,
+                                                       pool.k_centroid, pool.k_radius)
+    _check(L.bsa_score_select_padded(ctypes.byref(problem), ctypes.byref(params), _ptr(pc[0]),
+                                     _ptr(pc[1]), _ptr(pc[2]), _ptr(pc[3]), _ptr(scores),
+                                     _ptr(b.kv_idx), b.width, _ptr(b.scores), _ptr(b.bounds),
+                                     _ptr(b.gate), _ptr(b.workspace), b.workspace.numel(),
+                                     _stream(dev)))
+    return b
+
+
+def bsa_attention_fwd_padded(problem: Problem, q, k, v, kv_idx, softmax_scale=None, q_scale=None,
+                             k_scale=None, v_scale=None, want_lse=True, out=None, lse=None):
+    import torch
+    L = load_library()
+    S, Hq, D = q.shape
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty(S, Hq, D, dtype=torch.bfloat16, device=q.device)
+    if want_lse and lse is None:
+        lse = torch.empty(Hq, S, dtype=torch.float32, device=q.device)
+    _check(L.bsa_attention_fwd_padded(ctypes.byref(problem), _ptr(_u8(q)), _ptr(_u8(k)),
+                                      _ptr(_u8(v)), _ptr(q_scale), _ptr(k_scale), _ptr(v_scale),
+                                      _ptr(kv_idx), kv_idx.shape[1], float(softmax_scale),
+                                      _ptr(out), _ptr(lse) if want_lse else None,
+                                      _stream(q.device)))
+    return out, (lse if want_lse else None)
 
 
 def bsa_attention_fwd(problem: Problem, q, k, v, row_ptr, col_idx, softmax_scale=None,

@@ -114,6 +114,31 @@ int64_t capacity_bound(const bsa::Shape& sh, const bsa_select_params* s) {
   return per_unit * sh.U();
 }
 
+// The largest kept set any row can have under the parameters: the padded
+// list's width.
+int64_t padded_width(const bsa::Shape& sh, const bsa_select_params* s) {
+  int64_t width = 0;
+  const int64_t keff =
+      (int64_t)s->top_k * (s->gate != BSA_GATE_NONE ? (int64_t)s->gate_factor : 1);
+  for (int64_t i = 0; i < sh.nb; ++i) {
+    const int64_t nforced = (s->force_sink && i > 0) ? 2 : 1;
+    const int64_t nc = i + 1 - nforced;
+    int64_t kept = nforced;
+    if (s->mass_threshold > 0.f) {
+      kept += nc;
+    } else {
+      if (s->top_k > 0) kept += keff < nc ? keff : nc;
+      if (s->rescue_fraction > 0.0 && nc > 0) {
+        int64_t nr = (int64_t)std::ceil(s->rescue_fraction * (double)nc);
+        kept += nr < nc ? nr : nc;
+      }
+    }
+    kept = kept < i + 1 ? kept : i + 1;
+    width = kept > width ? kept : width;
+  }
+  return width;
+}
+
 bsa::SelectConfig select_config(const bsa_select_params* params) {
   bsa::SelectConfig cfg;
   cfg.top_k = params->top_k;
@@ -318,6 +343,91 @@ bsa_status bsa_select_scores(const bsa_problem* problem, const bsa_select_params
                                col_capacity, nullptr, nullptr, gate_out, workspace,
                                (hipStream_t)hip_stream, scores),
       "bsa_select_scores launch");
+}
+
+int64_t bsa_padded_width(const bsa_problem* problem, const bsa_select_params* params) {
+  bsa::Shape sh;
+  if (check_problem(problem, sh) != BSA_OK || check_params(params) != BSA_OK) return -1;
+  return padded_width(sh, params);
+}
+
+size_t bsa_score_select_padded_workspace_size(const bsa_problem* problem,
+                                              const bsa_select_params* params,
+                                              int scores_given_or_exported) {
+  bsa::Shape sh;
+  if (check_problem(problem, sh) != BSA_OK || check_params(params) != BSA_OK) return 0;
+  return bsa::select_workspace_layout(sh, scores_given_or_exported != 0,
+                                      params->gate == BSA_GATE_SIGMA_CUT)
+      .total;
+}
+
+bsa_status bsa_score_select_padded(const bsa_problem* problem, const bsa_select_params* params,
+                                   const float* q_centroid, const float* q_norm,
+                                   const float* k_centroid, const float* k_radius,
+                                   const float* scores_in, int32_t* kv_idx, int64_t width,
+                                   float* scores_out, float* bound_out, uint8_t* gate_out,
+                                   void* workspace, size_t workspace_bytes, void* hip_stream) {
+  bsa::Shape sh;
+  bsa_status st = check_problem(problem, sh);
+  if (st != BSA_OK) return st;
+  st = check_params(params);
+  if (st != BSA_OK) return st;
+  const bool rescue = params->rescue_fraction > 0.0;
+  if (scores_in && (rescue || scores_out || bound_out))
+    return fail(BSA_ERR_INVALID_ARGUMENT,
+                "with given scores there is no rescue branch and nothing to export");
+  if (sh.S == 0) return ok();
+  if (!kv_idx) return fail(BSA_ERR_INVALID_ARGUMENT, "kv_idx is required");
+  if (!scores_in && (!q_centroid || !k_centroid))
+    return fail(BSA_ERR_INVALID_ARGUMENT, "q_centroid and k_centroid are required");
+  if (misaligned(q_centroid) || misaligned(k_centroid) || misaligned(workspace))
+    return fail(BSA_ERR_INVALID_ARGUMENT,
+                "q_centroid, k_centroid and workspace must be 16-byte aligned");
+  if (rescue && (!q_norm || !k_radius))
+    return fail(BSA_ERR_INVALID_ARGUMENT, "the rescue branch needs q_norm and k_radius");
+  const int64_t need_w = padded_width(sh, params);
+  if (width < need_w)
+    return fail(BSA_ERR_CAPACITY, "width %lld < %lld kept blocks a row can have",
+                (long long)width, (long long)need_w);
+  if ((int64_t)sh.U() * sh.nb * width > 0x7FFFFFFF)
+    return fail(BSA_ERR_UNSUPPORTED, "padded list of %lld entries exceeds int32 indexing",
+                (long long)((int64_t)sh.U() * sh.nb * width));
+  const size_t need = bsa::select_workspace_layout(sh, scores_in || scores_out,
+                                                   params->gate == BSA_GATE_SIGMA_CUT)
+                          .total;
+  if (!workspace || workspace_bytes < need)
+    return fail(BSA_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, need);
+  const bsa::SelectConfig cfg = select_config(params);
+  return device_status(
+      bsa::launch_score_select(sh, cfg, q_centroid, rescue ? q_norm : nullptr, k_centroid,
+                               rescue ? k_radius : nullptr, nullptr, kv_idx, 0, scores_out,
+                               rescue ? bound_out : nullptr, gate_out, workspace,
+                               (hipStream_t)hip_stream, scores_in, (int)width),
+      "bsa_score_select_padded launch");
+}
+
+bsa_status bsa_attention_fwd_padded(const bsa_problem* problem, const void* q, const void* k,
+                                    const void* v, const float* q_scale, const float* k_scale,
+                                    const float* v_scale, const int32_t* kv_idx, int64_t width,
+                                    float softmax_scale, void* out, float* lse, void* hip_stream) {
+  bsa::Shape sh;
+  bsa_status st = check_problem(problem, sh);
+  if (st != BSA_OK) return st;
+  if (sh.S == 0) return ok();
+  if (!q || !k || !v || !kv_idx || !out)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "q, k, v, kv_idx and out are required");
+  if (sh.fp8 && (!q_scale || !k_scale || !v_scale))
+    return fail(BSA_ERR_INVALID_ARGUMENT, "FP8 inputs need q_scale, k_scale and v_scale");
+  if (!std::isfinite(softmax_scale) || softmax_scale <= 0.f)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and > 0");
+  if (width < 1 || width > sh.nb)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "width %lld outside [1, %d]", (long long)width, sh.nb);
+  if ((int64_t)sh.U() * sh.nb * width > 0x7FFFFFFF)
+    return fail(BSA_ERR_UNSUPPORTED, "padded list exceeds int32 indexing");
+  return device_status(bsa::launch_attention(sh, q, k, v, q_scale, k_scale, v_scale, nullptr,
+                                             kv_idx, softmax_scale, out, lse,
+                                             (hipStream_t)hip_stream, (int)width),
+                       "bsa_attention_fwd_padded launch");
 }
 
 bsa_status bsa_attention_fwd(const bsa_problem* problem, const void* q, const void* k,

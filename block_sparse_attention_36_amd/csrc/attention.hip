@@ -50,12 +50,13 @@ struct AttnArgs {
   const float* q_scale;
   const float* k_scale;
   const float* v_scale;
-  const int32_t* row_ptr;
+  const int32_t* row_ptr;  // CSR rows, or nullptr with the padded list
   const int32_t* col_idx;
   void* out;
   float* lse;
   int64_t S;
   int Hq, Hkv, nb, per_group;
+  int width;  // > 0: padded list, row r at col_idx[r*width], valid entries first
   float scale_log2;
 };
 
@@ -283,8 +284,17 @@ __global__ __launch_bounds__(64 * (B / 32), 2) void attn_whole_kernel(AttnArgs a
   const int h = g * G + hh;
   const int unit = a.per_group ? g : h;
   const int row = unit * nb + i;
-  const int e0 = a.row_ptr[row], e1 = a.row_ptr[row + 1];
-  const int nblk = e1 - e0;
+  int e0, nblk;
+  if (a.width > 0) {
+    // padded row: its valid entries (a prefix of the row) are counted by ballots
+    e0 = row * a.width;
+    nblk = 0;
+    for (int c = 0; c < a.width; c += 64)
+      nblk += __popcll(__ballot(c + l < a.width && a.col_idx[e0 + c + l] >= 0));
+  } else {
+    e0 = a.row_ptr[row];
+    nblk = a.row_ptr[row + 1] - e0;
+  }
 
   // kept block ids (and E4M3 scales) 64 at a time, lane L holding entry base + L,
   // read back with V_READLANE; -1 marks an entry outside the causal range, whose
@@ -516,7 +526,7 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
 hipError_t launch_attention(const Shape& sh, const void* q, const void* k, const void* v,
                             const float* q_scale, const float* k_scale, const float* v_scale,
                             const int32_t* row_ptr, const int32_t* col_idx, float softmax_scale,
-                            void* out, float* lse, hipStream_t stream) {
+                            void* out, float* lse, hipStream_t stream, int width) {
   AttnArgs a;
   a.q = q;
   a.k = k;
@@ -533,6 +543,7 @@ hipError_t launch_attention(const Shape& sh, const void* q, const void* k, const
   a.Hkv = sh.Hkv;
   a.nb = sh.nb;
   a.per_group = sh.per_group;
+  a.width = width;
   a.scale_log2 = softmax_scale * kLog2e;
 #define BSA_ATTN(DD, BB) \
   if (sh.D == DD && sh.B == BB) \

@@ -35,13 +35,14 @@ struct SelectWorkspace {
 SelectWorkspace select_workspace_layout(const Shape& sh, bool export_scores, bool sigma_gate);
 
 // scores_in != nullptr: selection on the given scores [U, nb, nb] (no centroid
-// scores are computed; q_centroid and k_centroid are unused).
+// scores are computed; q_centroid and k_centroid are unused).  width > 0: the
+// output is the padded list col_idx[rows][width] (row_ptr unused), else CSR.
 hipError_t launch_score_select(const Shape& sh, const SelectConfig& cfg, const float* q_centroid,
                                const float* q_norm, const float* k_centroid,
                                const float* k_radius, int32_t* row_ptr, int32_t* col_idx,
                                int64_t col_capacity, float* scores_out, float* bound_out,
                                uint8_t* gate_out, void* workspace, hipStream_t stream,
-                               const float* scores_in = nullptr);
+                               const float* scores_in = nullptr, int width = 0);
 
 hipError_t launch_key_bounds(const Shape& sh, const void* k, const float* k_scale, float* k_min,
                              float* k_max, hipStream_t stream);
@@ -51,9 +52,11 @@ hipError_t launch_quest_scores(const Shape& sh, const void* q, const float* q_sc
                                const float* k_min, const float* k_max, float* scores,
                                void* workspace, hipStream_t stream);
 
+// width > 0: col_idx is the padded list [rows][width] (valid entries first, then
+// -1) and row_ptr is unused; else CSR.
 hipError_t launch_attention(const Shape& sh, const void* q, const void* k, const void* v,
                             const float* q_scale, const float* k_scale, const float* v_scale,
                             const int32_t* row_ptr, const int32_t* col_idx, float softmax_scale,
-                            void* out, float* lse, hipStream_t stream);
+                            void* out, float* lse, hipStream_t stream, int width = 0);
 
 }  // namespace bsa

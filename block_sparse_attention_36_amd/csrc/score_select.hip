@@ -815,19 +815,25 @@ __global__ __launch_bounds__(256) void expand_counts_kernel(int* __restrict__ co
   if (row < rows && fire[row % nb]) counts[row] += counts_x[row];
 }
 
+// One wave per row writes the set bits of its mask in ascending order.  With the
+// sigma gate, rows of fired tiles add their expansion bits (disjoint from the
+// kept bits) and the row's gate flag is its tile's decision.  With width > 0 the
+// output is the padded list instead of CSR: row r occupies [r*width, (r+1)*width),
+// its blocks ascending and then -1 sentinels, with no scan.
 __global__ __launch_bounds__(256) void compact_kernel(const unsigned long long* __restrict__ mask,
                                                       const unsigned long long* __restrict__ mask_x,
                                                       const uint8_t* __restrict__ fire,
                                                       uint8_t* __restrict__ gate_out,
                                                       const int32_t* __restrict__ row_ptr,
                                                       int32_t* __restrict__ col_idx, int rows,
-                                                      int nb, int nw, int64_t capacity) {
+                                                      int nb, int nw, int64_t capacity, int width) {
   const int l = lane_id();
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
   const int i = row % nb;
   const int nslots = i / 64 + 1;
-  const int64_t base = row_ptr[row];
+  const int64_t base = width > 0 ? (int64_t)row * width : row_ptr[row];
+  if (width > 0) capacity = base + width;
   const bool expand = fire != nullptr && fire[i];
   if (fire != nullptr && gate_out != nullptr && l == 0) gate_out[row] = expand ? 1 : 0;
   int run = 0;
@@ -841,6 +847,8 @@ __global__ __launch_bounds__(256) void compact_kernel(const unsigned long long* 
     }
     run += __popcll(w);
   }
+  if (width > 0)
+    for (int p = run + l; p < width; p += 64) col_idx[base + p] = -1;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -880,7 +888,7 @@ hipError_t launch_score_select(const Shape& sh, const SelectConfig& cfg, const f
                                const float* k_radius, int32_t* row_ptr, int32_t* col_idx,
                                int64_t col_capacity, float* scores_out, float* bound_out,
                                uint8_t* gate_out, void* workspace, hipStream_t stream,
-                               const float* scores_in) {
+                               const float* scores_in, int width) {
   const bool sig = cfg.gate == 2 && cfg.top_k > 0;
   const SelectWorkspace w =
       select_workspace_layout(sh, scores_out != nullptr || scores_in != nullptr, cfg.gate == 2);
@@ -972,18 +980,20 @@ hipError_t launch_score_select(const Shape& sh, const SelectConfig& cfg, const f
     if (e != hipSuccess) return e;
   }  // (with the top-k branch off the select kernel writes gate_out = 0 itself)
 
-  if (fire) {
-    hipLaunchKernelGGL(expand_counts_kernel, dim3((rows + 255) / 256), dim3(256), 0, stream,
-                       counts, a.counts_x, fire, rows, nb);
+  if (width == 0) {
+    if (fire) {
+      hipLaunchKernelGGL(expand_counts_kernel, dim3((rows + 255) / 256), dim3(256), 0, stream,
+                         counts, a.counts_x, fire, rows, nb);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, stream, counts, row_ptr, rows,
+                       col_capacity);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, stream, counts, row_ptr, rows,
-                     col_capacity);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(compact_kernel, dim3((rows + 3) / 4), dim3(256), 0, stream, mask, a.mask_x,
-                     fire, gate_out, row_ptr, col_idx, rows, nb, nw, col_capacity);
+                     fire, gate_out, row_ptr, col_idx, rows, nb, nw, col_capacity, width);
   return hipGetLastError();
 }
 

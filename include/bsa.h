@@ -19,6 +19,9 @@
  *                        per query tile the maximum over its rows;
  *   bsa_select_scores    the selection rules of bsa_score_select on given scores.
  *
+ * Either selection can instead emit a uniform-width, sentinel-padded list
+ * (bsa_score_select_padded) that bsa_attention_fwd_padded consumes.
+ *
  * Sources (the method these calls compute):
  *   - "Uncertainty-gated selection for block-sparse attention" (gist.science),
  *     technical summary, Methodology steps 1-2 (block scores from mean-pooled
@@ -247,6 +250,52 @@ bsa_status bsa_select_scores(const bsa_problem* problem, const bsa_select_params
                              const float* scores, int32_t* row_ptr, int32_t* col_idx,
                              int64_t col_capacity, uint8_t* gate_out, void* workspace,
                              size_t workspace_bytes, void* hip_stream);
+
+/* Slots per row of the padded list: the largest kept set any row can have under
+ * the parameters (forced blocks plus rho*k or k by top-k, ceil(phi*|C|) by
+ * rescue, every candidate with the mass branch); -1 on invalid arguments. */
+int64_t bsa_padded_width(const bsa_problem* problem, const bsa_select_params* params);
+
+/* Workspace bytes of bsa_score_select_padded (scores_given_or_exported: 1 when
+ * scores_in or scores_out will be non-NULL); 0 on invalid arguments. */
+size_t bsa_score_select_padded_workspace_size(const bsa_problem* problem,
+                                              const bsa_select_params* params,
+                                              int scores_given_or_exported);
+
+/*
+ * bsa_score_select_padded -- the selection of bsa_score_select (centroid scores)
+ * or, with scores_in != NULL, of bsa_select_scores (given scores), written as a
+ * uniform list instead of CSR ("Uncertainty-gated selection ...", technical
+ * summary, Methodology step 5: one uniform dispatch shape, rows whose gate did
+ * not fire padded with sentinels).
+ *
+ *   kv_idx       out int32 [U*nb, width]: row r holds its kept blocks ascending
+ *                from kv_idx[r*width], then -1 to the end of the row.
+ *   width        at least bsa_padded_width(), else BSA_ERR_CAPACITY; U*nb*width
+ *                must fit int32 (BSA_ERR_UNSUPPORTED).
+ *   scores_in    NULL: centroid scores from q_centroid/k_centroid (as
+ *                bsa_score_select, exports allowed).  Otherwise the scores to
+ *                select on; then rescue_fraction must be 0 and scores_out,
+ *                bound_out NULL.
+ *   gate_out, workspace as in bsa_score_select (workspace of at least
+ *                bsa_score_select_padded_workspace_size() bytes).
+ */
+bsa_status bsa_score_select_padded(const bsa_problem* problem, const bsa_select_params* params,
+                                   const float* q_centroid, const float* q_norm,
+                                   const float* k_centroid, const float* k_radius,
+                                   const float* scores_in, int32_t* kv_idx, int64_t width,
+                                   float* scores_out, float* bound_out, uint8_t* gate_out,
+                                   void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * bsa_attention_fwd_padded -- bsa_attention_fwd on a padded list: row (u, i) is
+ * kv_idx[(u*nb + i)*width ...], its valid entries first (unique, in any order)
+ * and -1 after them; the sentinels cost nothing.  width in [1, nb].
+ */
+bsa_status bsa_attention_fwd_padded(const bsa_problem* problem, const void* q, const void* k,
+                                    const void* v, const float* q_scale, const float* k_scale,
+                                    const float* v_scale, const int32_t* kv_idx, int64_t width,
+                                    float softmax_scale, void* out, float* lse, void* hip_stream);
 
 /*
  * bsa_attention_fwd -- attention over the kept blocks (RBS-Attention, third

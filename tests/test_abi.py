@@ -184,6 +184,41 @@ def test_quest_entry_points_validate_before_launching(lib):
     assert b"rescue" in lib.bsa_last_error()
 
 
+def test_padded_width_matches_the_oracle_and_calls_validate(lib):
+    from oracle import bsa_oracle as O
+    for kw, okw in ((dict(top_k=32, force_sink=1, gate=bsa.BSA_GATE_SIGMA_CUT, gate_threshold=0.3),
+                     dict(top_k=32, force_sink=True, gate="sigma_cut", gate_threshold=0.3)),
+                    (dict(top_k=5), dict(top_k=5)),
+                    (dict(top_k=2, rescue_fraction=0.05), dict(top_k=2, rescue_fraction=0.05)),
+                    (dict(mass_threshold=0.9, rescue_fraction=0.05),
+                     dict(mass_threshold=0.9, rescue_fraction=0.05))):
+        for seq in (4096, 100 * 128 + 3, 300):
+            p = _prob(seq_len=seq)
+            s = bsa.make_params(**kw)
+            nb = lib.bsa_num_blocks(ctypes.byref(p))
+            w = lib.bsa_padded_width(ctypes.byref(p), ctypes.byref(s))
+            assert w == O.padded_width(nb, O.SelectParams(**okw).as_library_precision())
+    p = _prob()
+    s = bsa.make_params(top_k=4, force_sink=1)
+    w = lib.bsa_padded_width(ctypes.byref(p), ctypes.byref(s))
+    ws = lib.bsa_score_select_padded_workspace_size(ctypes.byref(p), ctypes.byref(s), 0)
+    st = lib.bsa_score_select_padded(ctypes.byref(p), ctypes.byref(s), FAKE, None, FAKE, None,
+                                     None, FAKE, w - 1, None, None, None, FAKE, ws, None)
+    assert st == 3
+    st = lib.bsa_score_select_padded(ctypes.byref(p), ctypes.byref(s), FAKE, None, FAKE, None,
+                                     None, FAKE, w, None, None, None, FAKE, ws - 1, None)
+    assert st == 4
+    sr = bsa.make_params(top_k=4, rescue_fraction=0.05)
+    st = lib.bsa_score_select_padded(ctypes.byref(p), ctypes.byref(sr), None, FAKE, None, FAKE,
+                                     FAKE, FAKE, 10**4, None, None, None, FAKE, 10**12, None)
+    assert st == 1  # given scores and a rescue branch
+    nb = lib.bsa_num_blocks(ctypes.byref(p))
+    for width in (0, nb + 1):
+        st = lib.bsa_attention_fwd_padded(ctypes.byref(p), FAKE, FAKE, FAKE, None, None, None,
+                                          FAKE, width, 0.1, FAKE, None, None)
+        assert st == 1
+
+
 def test_attention_rejects_bad_arguments(lib):
     p = _prob()
     st = lib.bsa_attention_fwd(ctypes.byref(p), FAKE, FAKE, None, None, None, None, FAKE, FAKE,

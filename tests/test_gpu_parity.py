@@ -115,6 +115,42 @@ def test_quest_backbone_parity(cfg):
     assert rep.ambiguous_rows <= max(1, rep.rows_checked // 100)
 
 
+# the padded list against CSR: the same selection, sentinels after each row's
+# blocks, and attention bitwise equal to the CSR run (same blocks, same order)
+PADDED = [scaled(config_by_name(n), 4096 + 77, num_q_heads=8, num_kv_heads=2, name=f"padded-{n}")
+          for n in ("gqa32k", "gated64k", "sigma64k", "quest64k", "dual128k")]
+
+
+@pytest.mark.parametrize("cfg", PADDED, ids=[c.name for c in PADDED])
+def test_padded_list_matches_csr(cfg):
+    _gpu_or_skip()
+    import block_sparse_attention_36_amd as bsa
+    import bsa_check as K
+    from oracle import bsa_oracle as O
+    print(f"[padded] {cfg.name} S={cfg.seq_len}", flush=True)
+    inp = generate(cfg, "cpu").to("cuda")
+    run = K.run_gpu(cfg, inp)
+    problem = bsa.make_problem(inp.q, inp.k, cfg.block_size, K.granularity_code(cfg))
+    params = K.lib_params(cfg)
+    if cfg.backbone == "quest":
+        pb = bsa.bsa_score_select_padded(problem, params, scores=run.scores, export=True)
+    else:
+        pool = bsa.bsa_pool(problem, inp.q, inp.k, inp.q_scale, inp.k_scale)
+        pb = bsa.bsa_score_select_padded(problem, params, pool=pool, export=True)
+    out, lse = bsa.bsa_attention_fwd_padded(problem, inp.q, inp.k, inp.v, pb.kv_idx,
+                                            1.0 / math.sqrt(cfg.head_dim), inp.q_scale,
+                                            inp.k_scale, inp.v_scale)
+    torch.cuda.synchronize()
+    U, nb = cfg.num_units, cfg.num_blocks
+    kept = O.from_csr(run.row_ptr, run.col_idx, U, nb)
+    width = O.padded_width(nb, K.params_of(cfg))
+    assert pb.width == width
+    assert np.array_equal(pb.kv_idx.cpu().numpy(), O.to_padded(kept, width))
+    assert np.array_equal(pb.gate.cpu().numpy(), run.gate)
+    assert torch.equal(out, run.out) and torch.equal(lse, run.lse)
+    print(f"  width={width} rows={U * nb} fired={int(run.gate.sum())}", flush=True)
+
+
 MID = [scaled(config_by_name("msa1m"), 2000 * 128 + 17, num_q_heads=4, num_kv_heads=2),
        scaled(config_by_name("dual128k"), 4000 * 128 - 3, num_q_heads=2, num_kv_heads=1),
        scaled(config_by_name("gated64k"), 3000 * 128, num_q_heads=2, num_kv_heads=1),
