@@ -202,6 +202,9 @@ bsa_status bsa_pool(const bsa_problem* problem, const void* q, const void* k,
     return fail(BSA_ERR_INVALID_ARGUMENT, "q, k, q_centroid and k_centroid are required");
   if (sh.fp8 && (!q_scale || !k_scale))
     return fail(BSA_ERR_INVALID_ARGUMENT, "FP8 inputs need q_scale and k_scale");
+  if (misaligned(q) || misaligned(k) || misaligned(q_centroid) || misaligned(k_centroid))
+    return fail(BSA_ERR_INVALID_ARGUMENT,
+                "q, k, q_centroid and k_centroid must be 16-byte aligned");
   return device_status(bsa::launch_pool(sh, q, k, sh.fp8 ? q_scale : nullptr,
                                         sh.fp8 ? k_scale : nullptr, q_centroid, q_norm,
                                         k_centroid, k_radius, (hipStream_t)hip_stream),
@@ -424,6 +427,8 @@ bsa_status bsa_attention_fwd_padded(const bsa_problem* problem, const void* q, c
     return fail(BSA_ERR_INVALID_ARGUMENT, "width %lld outside [1, %d]", (long long)width, sh.nb);
   if ((int64_t)sh.U() * sh.nb * width > 0x7FFFFFFF)
     return fail(BSA_ERR_UNSUPPORTED, "padded list exceeds int32 indexing");
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(out))
+    return fail(BSA_ERR_INVALID_ARGUMENT, "q, k, v and out must be 16-byte aligned");
   return device_status(bsa::launch_attention(sh, q, k, v, q_scale, k_scale, v_scale, nullptr,
                                              kv_idx, softmax_scale, out, lse,
                                              (hipStream_t)hip_stream, (int)width),
@@ -445,6 +450,8 @@ bsa_status bsa_attention_fwd(const bsa_problem* problem, const void* q, const vo
     return fail(BSA_ERR_INVALID_ARGUMENT, "FP8 inputs need q_scale, k_scale and v_scale");
   if (!std::isfinite(softmax_scale) || softmax_scale <= 0.f)
     return fail(BSA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and > 0");
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(out))
+    return fail(BSA_ERR_INVALID_ARGUMENT, "q, k, v and out must be 16-byte aligned");
   return device_status(bsa::launch_attention(sh, q, k, v, q_scale, k_scale, v_scale, row_ptr,
                                              col_idx, softmax_scale, out, lse,
                                              (hipStream_t)hip_stream),

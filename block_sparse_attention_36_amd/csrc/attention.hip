@@ -36,6 +36,8 @@
 // read raw from LDS and Q held raw in registers; V is expanded to bf16 in LDS
 // (exact) for O^T = V^T P^T.  q_scale and k_scale fold into the per-block logit
 // scale and v_scale into the probabilities.
+#include <atomic>
+
 #include "common.h"
 #include "launch.h"
 
@@ -510,11 +512,17 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
   static_assert(WT::LDS_BYTES <= 80 * 1024, "two workgroups per CU must fit the 160 KiB LDS");
   const int G = a.Hq / a.Hkv;
   const int rows8 = (a.Hkv * a.nb + 7) / 8;
-  static bool attr_set = false;
-  if (!attr_set) {
-    (void)hipFuncSetAttribute((const void*)attn_whole_kernel<D, B, FP8>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, WT::LDS_BYTES);
-    attr_set = true;
+  // the LDS limit is raised once per device (64 KiB and more need the attribute)
+  static std::atomic<uint64_t> attr_set{0};
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  const uint64_t bit = 1ull << (dev & 63);
+  if (!(attr_set.load(std::memory_order_acquire) & bit)) {
+    const hipError_t e = hipFuncSetAttribute((const void*)attn_whole_kernel<D, B, FP8>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             WT::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    attr_set.fetch_or(bit, std::memory_order_acq_rel);
   }
   hipLaunchKernelGGL((attn_whole_kernel<D, B, FP8>), dim3(rows8 * 8 * G), dim3(WCfg<D, B>::NT),
                      WT::LDS_BYTES, stream, a);

@@ -219,6 +219,16 @@ def test_padded_width_matches_the_oracle_and_calls_validate(lib):
         assert st == 1
 
 
+def test_misaligned_pointers_are_rejected_before_launch(lib):
+    p = _prob()
+    odd = ctypes.c_void_p(0x1002)
+    assert lib.bsa_pool(ctypes.byref(p), odd, FAKE, None, None, FAKE, None, FAKE, None, None) == 1
+    assert b"aligned" in lib.bsa_last_error()
+    assert lib.bsa_attention_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, None, None, None, FAKE, FAKE,
+                                 0.1, odd, None, None) == 1
+    assert lib.bsa_pool_key_bounds(ctypes.byref(p), odd, None, FAKE, FAKE, None) == 1
+
+
 def test_attention_rejects_bad_arguments(lib):
     p = _prob()
     st = lib.bsa_attention_fwd(ctypes.byref(p), FAKE, FAKE, None, None, None, None, FAKE, FAKE,
