@@ -35,6 +35,12 @@ def _small(name):
 
 
 SMALL = [s for c in CONFIGS for s in _small(c.name)]
+# the sigma gate beside the mass and rescue branches (one union), and on
+# per-group E4M3 rows (one list per GQA group)
+SMALL += [scaled(config_by_name("dual128k"), 4096 + 77, num_q_heads=8, num_kv_heads=2, top_k=8,
+                 gate="sigma_cut", gate_threshold=0.3, name="sigma-with-mass-and-rescue"),
+          scaled(config_by_name("msa1m"), 8192 + 1, num_q_heads=16, num_kv_heads=2, top_k=16,
+                 gate="sigma_cut", gate_threshold=0.3, name="sigma-per-group-fp8")]
 # every supported (head_dim, block_size) pair in both input formats, ragged tails
 SHAPES = [scaled(config_by_name(base), 4096 + tail, num_q_heads=8, num_kv_heads=2,
                  head_dim=d, block_size=b, name=f"{base}-D{d}-B{b}")
