@@ -67,20 +67,55 @@ __device__ __forceinline__ unsigned float_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// All-lane wave reductions without the LDS crossbar: DPP moves pair lanes inside
+// each 16-lane row (quad_perm [1,0,3,2] and [2,3,0,1], then the 8- and 16-lane
+// mirrors), V_PERMLANE16_SWAP pairs rows 0-1 and 2-3, V_PERMLANE32_SWAP the two
+// halves.  Each swap of x with itself returns, in its two results, every lane's
+// own value and its partner's, so combining them reduces the pair in all lanes.
+// Every lane combines the same two partial values at every step (in one order or
+// the other, which commutative operations do not see), so all lanes end with the
+// same bits, and the fixed tree makes results reproducible run to run.
+#define BSA_DPP(x, ctrl) __builtin_amdgcn_update_dpp((x), (x), (ctrl), 0xF, 0xF, false)
+
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_allreduce(T x, Op op) {
+  static_assert(sizeof(T) == 4, "32-bit lanes");
+  auto bits = [](T v) { return __builtin_bit_cast(int, v); };
+  auto val = [](int v) { return __builtin_bit_cast(T, v); };
+  x = op(x, val(BSA_DPP(bits(x), 0xB1)));   // quad_perm [1,0,3,2]
+  x = op(x, val(BSA_DPP(bits(x), 0x4E)));   // quad_perm [2,3,0,1]
+  x = op(x, val(BSA_DPP(bits(x), 0x141)));  // row_half_mirror
+  x = op(x, val(BSA_DPP(bits(x), 0x140)));  // row_mirror
+  const auto r16 = __builtin_amdgcn_permlane16_swap((unsigned)bits(x), (unsigned)bits(x), false,
+                                                    false);
+  x = op(val((int)r16[0]), val((int)r16[1]));
+  const auto r32 = __builtin_amdgcn_permlane32_swap((unsigned)bits(x), (unsigned)bits(x), false,
+                                                    false);
+  return op(val((int)r32[0]), val((int)r32[1]));
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
-  // fixed butterfly: the same tree on every call, so results are reproducible
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-  return x;
+  return wave_allreduce(x, [](float a, float b) { return a + b; });
 }
 
 __device__ __forceinline__ float wave_max(float x) {
-  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
+  return wave_allreduce(x, [](float a, float b) { return fmaxf(a, b); });
 }
 
 __device__ __forceinline__ int wave_sum_int(int x) {
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-  return x;
+  return wave_allreduce(x, [](int a, int b) { return a + b; });
+}
+
+__device__ __forceinline__ int wave_min_int(int x) {
+  return wave_allreduce(x, [](int a, int b) { return a < b ? a : b; });
+}
+
+__device__ __forceinline__ unsigned wave_max_uint(unsigned x) {
+  return wave_allreduce(x, [](unsigned a, unsigned b) { return a > b ? a : b; });
+}
+
+__device__ __forceinline__ unsigned wave_min_uint(unsigned x) {
+  return wave_allreduce(x, [](unsigned a, unsigned b) { return a < b ? a : b; });
 }
 
 __device__ __forceinline__ unsigned long long ballot64(bool p) { return __ballot(p); }

@@ -123,15 +123,9 @@ __device__ __forceinline__ float key_float(unsigned k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-__device__ __forceinline__ unsigned wave_max_u(unsigned x) {
-  for (int o = 32; o >= 1; o >>= 1) x = max(x, (unsigned)__shfl_xor((int)x, o));
-  return x;
-}
+__device__ __forceinline__ unsigned wave_max_u(unsigned x) { return wave_max_uint(x); }
 
-__device__ __forceinline__ unsigned wave_min_u(unsigned x) {
-  for (int o = 32; o >= 1; o >>= 1) x = min(x, (unsigned)__shfl_xor((int)x, o));
-  return x;
-}
+__device__ __forceinline__ unsigned wave_min_u(unsigned x) { return wave_min_uint(x); }
 
 // Cut margin of a top-k decision from the keys of s(0) (best candidate), s(k-1)
 // (last kept) and s(k) (first dropped): (s(k-1) - s(k)) / (s(0) - s(k)), and 0
@@ -265,7 +259,7 @@ __global__ __launch_bounds__(256) void select_kernel(SelArgs a) {
         const int j = e * 64 + l;
         if (is_cand(j, i, sink) && s[j] == s0) jmax = min(jmax, j);
       }
-      for (int o = 32; o >= 1; o >>= 1) jmax = min(jmax, __shfl_xor(jmax, o));
+      jmax = wave_min_int(jmax);
       float m2 = -INFINITY;
       for (int e = 0; e < nslots; ++e) {
         const int j = e * 64 + l;
@@ -495,7 +489,7 @@ __global__ __launch_bounds__(256) void select_reg_kernel(SelArgs a) {
 #pragma unroll
     for (int e = 0; e < SPL; ++e)
       if (e < nsl && sr.cand(e)) km = max(km, sr.k[e]);
-    for (int o = 32; o >= 1; o >>= 1) km = max(km, (unsigned)__shfl_xor((int)km, o));
+    km = wave_max_uint(km);
     kmax = km;
     s0 = key_float(kmax);
     float z = 0.f;
@@ -515,12 +509,12 @@ __global__ __launch_bounds__(256) void select_reg_kernel(SelArgs a) {
 #pragma unroll
       for (int e = SPL - 1; e >= 0; --e)
         if (e < nsl && sr.cand(e) && sr.k[e] == kmax) jm = e * 64 + l;
-      for (int o = 32; o >= 1; o >>= 1) jm = min(jm, __shfl_xor(jm, o));
+      jm = wave_min_int(jm);
       unsigned k2 = 0u;
 #pragma unroll
       for (int e = 0; e < SPL; ++e)
         if (e < nsl && sr.cand(e) && e * 64 + l != jm) k2 = max(k2, sr.k[e]);
-      for (int o = 32; o >= 1; o >>= 1) k2 = max(k2, (unsigned)__shfl_xor((int)k2, o));
+      k2 = wave_max_uint(k2);
       const float gap = (1.0f - exp2f((key_float(k2) - s0) * a.tau_log2e)) / zsum;
       fired = gap < a.gate_threshold;
     }
@@ -550,14 +544,11 @@ __global__ __launch_bounds__(256) void select_reg_kernel(SelArgs a) {
           bk = sr.k[e];
           bj = e * 64 + l;
         }
-      for (int o = 32; o >= 1; o >>= 1) {
-        const unsigned ok = (unsigned)__shfl_xor((int)bk, o);
-        const int oj = __shfl_xor(bj, o);
-        if (ok > bk || (ok == bk && oj < bj)) {
-          bk = ok;
-          bj = oj;
-        }
-      }
+      // the largest key, then the lowest block index holding it (each lane's bj is
+      // its lowest slot with its own largest key)
+      const unsigned kb = wave_max_uint(bk);
+      bj = wave_min_int(bk == kb ? bj : 0x7FFFFFFF);
+      bk = kb;
       if (bj == 0x7FFFFFFF) break;  // every candidate taken
       cum += exp2f((key_float(bk) - s0) * a.tau_log2e) / zsum;
       if ((bj & 63) == l) taken.set(bj >> 6);
