@@ -407,13 +407,14 @@ struct RowKeys {
   __device__ __forceinline__ bool cand(int e) const { return cand_bits.get(e); }
 };
 
-// number of candidates with key >= x (wave-uniform)
+// number of candidates with key >= x (wave-uniform).  Slots that hold no
+// candidate keep key 0, below every probe (x >= 1), so no candidacy test is needed.
 template <int SPL>
 __device__ __forceinline__ int count_ge_reg(const RowKeys<SPL>& r, int nsl, unsigned x) {
   int c = 0;
 #pragma unroll
   for (int e = 0; e < SPL; ++e)
-    if (e < nsl) c += __popcll(ballot64(r.cand(e) && r.k[e] >= x));
+    if (e < nsl) c += __popcll(ballot64(r.k[e] >= x));
   return c;
 }
 
@@ -474,7 +475,12 @@ __global__ __launch_bounds__(256) void select_reg_kernel(SelArgs a) {
         br.k[e] = float_key(bv);
         if (a.bound_out) a.bound_out[((size_t)u * nb + i) * nb + j] = bv;
       }
-      if (is_cand(j, i, sink)) sr.cand_bits.set(e);
+      if (is_cand(j, i, sink)) {
+        sr.cand_bits.set(e);
+      } else {
+        sr.k[e] = 0u;  // forced blocks are no candidates: below every probe
+        br.k[e] = 0u;
+      }
     }
   }
   br.cand_bits = sr.cand_bits;
