@@ -462,24 +462,42 @@ __global__ __launch_bounds__(256) void select_reg_kernel(SelArgs a) {
 
   RowKeys<SPL> sr, br;
   sr.cand_bits.clear();
+  // the row is read in chunks of up to 16 slots per lane, each chunk's loads issued
+  // together (indices clamped into the row, one wait per chunk) rather than one
+  // load and one wait per slot
+  constexpr int CH = SPL <= 16 ? SPL : 8;
 #pragma unroll
-  for (int e = 0; e < SPL; ++e) {
-    sr.k[e] = 0u;
-    br.k[e] = 0u;
-    const int j = e * 64 + l;
-    if (e < nsl && j <= i) {
-      const float sv = srow[j];
-      sr.k[e] = float_key(sv);
-      if (use_b) {
-        const float bv = fmaf(qnv, a.kr[(size_t)g * nb + j], sv);
-        br.k[e] = float_key(bv);
-        if (a.bound_out) a.bound_out[((size_t)u * nb + i) * nb + j] = bv;
+  for (int e0 = 0; e0 < SPL; e0 += CH) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      sr.k[e0 + c] = 0u;
+      br.k[e0 + c] = 0u;
+    }
+    if (e0 < nsl) {
+      float sv[CH], kv[CH];
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        const int j = min((e0 + c) * 64 + l, i);
+        sv[c] = srow[j];
+        if (use_b) kv[c] = a.kr[(size_t)g * nb + j];
       }
-      if (is_cand(j, i, sink)) {
-        sr.cand_bits.set(e);
-      } else {
-        sr.k[e] = 0u;  // forced blocks are no candidates: below every probe
-        br.k[e] = 0u;
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        const int e = e0 + c, j = e * 64 + l;
+        if (e < nsl && j <= i) {
+          sr.k[e] = float_key(sv[c]);
+          if (use_b) {
+            const float bv = fmaf(qnv, kv[c], sv[c]);
+            br.k[e] = float_key(bv);
+            if (a.bound_out) a.bound_out[((size_t)u * nb + i) * nb + j] = bv;
+          }
+          if (is_cand(j, i, sink)) {
+            sr.cand_bits.set(e);
+          } else {
+            sr.k[e] = 0u;  // forced blocks are no candidates: below every probe
+            br.k[e] = 0u;
+          }
+        }
       }
     }
   }
