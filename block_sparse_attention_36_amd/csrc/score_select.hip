@@ -409,12 +409,18 @@ struct RowKeys {
 
 // number of candidates with key >= x (wave-uniform).  Slots that hold no
 // candidate keep key 0, below every probe (x >= 1), so no candidacy test is needed.
+// Slots past the row (e >= nsl) hold key 0 as well, so the row is counted in
+// chunks of 8 slots behind one uniform branch each.
 template <int SPL>
 __device__ __forceinline__ int count_ge_reg(const RowKeys<SPL>& r, int nsl, unsigned x) {
+  constexpr int CH = SPL < 8 ? SPL : 8;
   int c = 0;
 #pragma unroll
-  for (int e = 0; e < SPL; ++e)
-    if (e < nsl) c += __popcll(ballot64(r.k[e] >= x));
+  for (int e0 = 0; e0 < SPL; e0 += CH)
+    if (e0 < nsl) {
+#pragma unroll
+      for (int e = e0; e < e0 + CH; ++e) c += __popcll(ballot64(r.k[e] >= x));
+    }
   return c;
 }
 
@@ -449,7 +455,9 @@ template <int SPL, bool FULL, bool SIG>
 __global__ __launch_bounds__(256) void select_reg_kernel(SelArgs a) {
   const bool use_b = FULL && a.use_b, use_p = FULL && a.use_p;
   const int l = lane_id();
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  // (the wave index through readfirstlane: row, i and the slot count are then
+  // known to be wave-uniform, and the per-slot conditions below scalar branches)
+  const int row = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (row >= a.rows) return;  // no workgroup barriers below
   const int nb = a.nb;
   const int u = row / nb, i = row % nb;
