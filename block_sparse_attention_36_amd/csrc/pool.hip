@@ -176,7 +176,7 @@ __global__ __launch_bounds__(64 * KW) void pool_k_kernel(
   __shared__ f32x4 part[KW][64][2];
   __shared__ float pmax[KW][64];
   const int j = blockIdx.x;
-  const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int l = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int gl = (l * 8) / D, d = (l * 8) % D;
   const int g = blockIdx.y * HW + gl;
   const bool active = gl < HW && g < Hkv;
@@ -257,7 +257,7 @@ __global__ __launch_bounds__(64 * KW) void kbounds_kernel(
   __shared__ f32x4 pmin[KW][64][2];
   __shared__ f32x4 pmax[KW][64][2];
   const int j = blockIdx.x;
-  const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int l = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int gl = (l * 8) / D, d = (l * 8) % D;
   const int g = blockIdx.y * HW + gl;
   const bool active = gl < HW && g < Hkv;

@@ -51,7 +51,7 @@ __global__ __launch_bounds__(256) void score_kernel(const float* __restrict__ qc
   const int it = blockIdx.x, jt = blockIdx.y, u = blockIdx.z;
   if (jt > it) return;  // uniform for the workgroup
   __shared__ float As[64 * 33], Bs[64 * 33];
-  const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, l = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wi = w >> 1, wj = w & 1, hf = l >> 5;
   const int g = per_group ? u : u / G;
   f32x16 acc = {0};
@@ -189,7 +189,7 @@ __device__ float mass_ge(const float* s, const float* p, int nslots, int i, int 
 __global__ __launch_bounds__(256) void select_kernel(SelArgs a) {
   extern __shared__ float sm[];
   const int l = lane_id();
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row = blockIdx.x * (blockDim.x >> 6) + wave;
   if (row >= a.rows) return;  // no workgroup barriers below
   const int nb = a.nb;
@@ -851,7 +851,7 @@ __global__ __launch_bounds__(256) void compact_kernel(const unsigned long long* 
                                                       int32_t* __restrict__ col_idx, int rows,
                                                       int nb, int nw, int64_t capacity, int width) {
   const int l = lane_id();
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int row = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (row >= rows) return;
   const int i = row % nb;
   const int nslots = i / 64 + 1;
