@@ -171,16 +171,25 @@ __global__ __launch_bounds__(64 * (B / 32), 2) void quest_score_kernel(QuestArgs
     for (int c = 0; c < nch; ++c) {
       const int cur = c & 1;
       if (c + 1 < nch) stage_load(c + 1);
-      f32x16 acc = {};
+      // bf16 bounds: two accumulators (even and odd contraction steps), independent
+      // product chains; the split bounds' longer contraction keeps one (and the
+      // occupancy its registers allow)
+      constexpr int NA = NP == 2 ? 2 : 1;
+      f32x16 accs[NA];
+#pragma unroll
+      for (int q = 0; q < NA; ++q) accs[q] = f32x16{0};
       const unsigned char* bb = lds + cur * C::BUF + (l & 31) * C::LROW + 16 * (l >> 5);
 #pragma unroll
       for (int s = 0; s < C::KSTEPS; ++s) {
         const u32x4 bf = *(const u32x4*)(bb + 32 * s);
         const u32x4 af = ((s / C::NS) & 1) ? qn[s % C::NS] : qp[s % C::NS];
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af),
-                                                      __builtin_bit_cast(bf16x8, bf), acc, 0, 0,
-                                                      0);
+        accs[s % NA] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af),
+                                                               __builtin_bit_cast(bf16x8, bf),
+                                                               accs[s % NA], 0, 0, 0);
       }
+      f32x16 acc = accs[0];
+#pragma unroll
+      for (int q = 1; q < NA; ++q) acc += accs[q];
       // maximum over this wave's valid rows, for column (block) 32c + (l & 31)
       float m = -INFINITY;
 #pragma unroll
