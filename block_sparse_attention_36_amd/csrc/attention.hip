@@ -19,9 +19,12 @@
 //
 // Memory and occupancy: a workgroup holds one K tile and one V tile in LDS
 // (64 KiB at D = B = 128), filled by direct global->LDS DMA, so two workgroups
-// share each CU: the two waves on a SIMD then belong to independent rows and run
-// out of phase (one's softmax on the VALU beside the other's products), and one
-// row's set-up and memory waits are covered by the other's products.  Within a
+// share each CU: the two waves on a SIMD then belong to independent rows, and one
+// row's set-up and memory waits are covered by the other's products.  Left alone
+// the two waves fall into step (both in their products, then both in their
+// softmax); a wave raises its priority from its row maximum through O += V P and
+// lowers it for the next block's products, which keeps them out of phase (one's
+// softmax on the VALU beside the other's products).  Within a
 // block, K(n+1) streams in while O += V(n) P(n) runs, and V(n+1) while S(n+1)
 // and its softmax run (two barriers per block).  LDS rows are XOR-swizzled in
 // 16-byte chunks so that both the 16-byte K reads (32 rows, one column) and the
@@ -426,6 +429,12 @@ __global__ __launch_bounds__(64 * (B / 32), 2) void attn_whole_kernel(AttnArgs a
                                                                    0, 127, 0, 127);
       }
     }
+    // Wave priority: the two waves on a SIMD run the same phases and, left to
+    // themselves, fall into step, so that their products and their softmax
+    // arithmetic serialise.  From the row maximum through O += V P this wave asks
+    // for the issue slots first; for the next block's request and products it
+    // yields, so a wave in its softmax runs ahead of one in its products.
+    __builtin_amdgcn_s_setprio(2);
     const float sl = a.scale_log2 * qsc * ksc;
     float mx = -INFINITY;
     if (j < 0 || j == i || (int64_t)j * B + B > a.S) {
@@ -482,6 +491,7 @@ __global__ __launch_bounds__(64 * (B / 32), 2) void attn_whole_kernel(AttnArgs a
     for (int kt2 = 0; kt2 < C::NKT; ++kt2) pv_tile<D, B>(vt + vrow0, pk[kt2], o, kt2, rlo, cb0);
 
     // ---- K(n + 1) has landed everywhere and V(n) is free: request V(n + 1)
+    __builtin_amdgcn_s_setprio(0);
     wait_vmem_all();
     lds_barrier();
     if (n + 1 < nblk) ST::issue(a, a.v, g, jn, lds + ST::VBUF, wave, doff);
