@@ -122,10 +122,11 @@ CONFIGS = [
 # The same router on the Quest backbone, the pairing behind the page's LongBench-v2
 # result: K-min/K-max per key block, per-row upper bounds, a tile's score the
 # maximum over its rows (same page, Methodology steps 1-2 and Results).
+_BASE = {c.name: c for c in CONFIGS}
 EXTRA_CONFIGS = [
-    dataclasses.replace(CONFIGS[3], name="dual128k_fp8", dtype="fp8"),
-    dataclasses.replace(CONFIGS[2], name="sigma64k", gate="sigma_cut", gate_threshold=0.30),
-    dataclasses.replace(CONFIGS[2], name="quest64k", gate="sigma_cut", gate_threshold=0.30,
+    dataclasses.replace(_BASE["dual128k"], name="dual128k_fp8", dtype="fp8"),
+    dataclasses.replace(_BASE["gated64k"], name="sigma64k", gate="sigma_cut", gate_threshold=0.30),
+    dataclasses.replace(_BASE["gated64k"], name="quest64k", gate="sigma_cut", gate_threshold=0.30,
                         backbone="quest"),
 ]
 
