@@ -280,6 +280,39 @@ def summarize_pmc(fetch_dir: str, write_dir: str, out_json: str) -> int:
     return 0
 
 
+def dense_context(bsa, torch, problem, cfg, inp, scale, out, lse, attn_ms: float,
+                  step_ms: float) -> dict:
+    """The same attention kernel on the full causal mask of the same problem (every
+    row keeps blocks 0..i): the dense prefill the sparse step stands against.
+    Context, not a target; run after the timed steps, so nothing here is timed in them."""
+    dev = out.device
+    nb, U = cfg.num_blocks, cfg.num_units
+    counts = (torch.arange(nb, device=dev, dtype=torch.int64) + 1).repeat(U)
+    rp = torch.zeros(U * nb + 1, dtype=torch.int64, device=dev)
+    rp[1:] = torch.cumsum(counts, 0)
+    row_of = torch.repeat_interleave(torch.arange(U * nb, device=dev), counts)
+    ci = (torch.arange(int(rp[-1]), device=dev, dtype=torch.int64) - rp[:-1][row_of]).to(torch.int32)
+    rp = rp.to(torch.int32)
+    del row_of
+    run = lambda: bsa.bsa_attention_fwd(problem, inp.q, inp.k, inp.v, rp, ci, scale, inp.q_scale,
+                                        inp.k_scale, inp.v_scale, out=out, lse=lse)
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(2):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 2
+    flops = dense_causal_flops(cfg)
+    return {"dense_attention_ms": round(ms, 3),
+            "dense_attention_tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+            "dense_attention_frac_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "speedup_sparse_attention": round(ms / attn_ms, 2),
+            "speedup_sparse_step": round(ms / step_ms, 2)}
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -290,6 +323,9 @@ def main(argv=None) -> int:
     ap.add_argument("--index-format", choices=("csr", "padded"), default="csr",
                     help="kept-block lists as CSR, or as the uniform sentinel-padded list")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--dense-context", action="store_true",
+                    help="after timing, run the same attention kernel on the full causal mask "
+                         "(dense prefill, context: speedup of the sparse step over it)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run one plain device copy of 1 GiB (counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT_JSON"),
@@ -298,6 +334,10 @@ def main(argv=None) -> int:
     args = ap.parse_args(argv)
     if args.summarize_pmc:
         return summarize_pmc(*args.summarize_pmc)
+    if args.dense_context and args.calibrate_copy:
+        print("--dense-context adds attention launches that --calibrate-copy counter runs "
+              "would average in; use one or the other", file=sys.stderr)
+        return 2
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (asked for {args.gpus}): the block-sparse "
               "prefill path here has no multi-GPU mode.", file=sys.stderr)
@@ -469,6 +509,10 @@ def main(argv=None) -> int:
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.dense_context:
+        print("[bench] dense causal attention (context)", file=sys.stderr, flush=True)
+        res["dense_context"] = dense_context(bsa, torch, problem, cfg, inp, scale, out, lse,
+                                             attn_avg, ms_per_step)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(cfg, inp, None, args.cpu_seconds)
