@@ -410,7 +410,9 @@ struct RowKeys {
 // number of candidates with key >= x (wave-uniform).  Slots that hold no
 // candidate keep key 0, below every probe (x >= 1), so no candidacy test is needed.
 // Slots past the row (e >= nsl) hold key 0 as well, so the row is counted in
-// chunks of 8 slots behind one uniform branch each.
+// chunks of 8 slots behind one uniform branch each.  The widest forms (64 and 128
+// slots, one wave per SIMD) count per lane on the VALU and sum the lanes once;
+// the others take a ballot popcount per slot on the scalar unit.
 template <int SPL>
 __device__ __forceinline__ int count_ge_reg(const RowKeys<SPL>& r, int nsl, unsigned x) {
   constexpr int CH = SPL < 8 ? SPL : 8;
@@ -419,8 +421,14 @@ __device__ __forceinline__ int count_ge_reg(const RowKeys<SPL>& r, int nsl, unsi
   for (int e0 = 0; e0 < SPL; e0 += CH)
     if (e0 < nsl) {
 #pragma unroll
-      for (int e = e0; e < e0 + CH; ++e) c += __popcll(ballot64(r.k[e] >= x));
+      for (int e = e0; e < e0 + CH; ++e) {
+        if constexpr (SPL >= 64)
+          c += r.k[e] >= x ? 1 : 0;
+        else
+          c += __popcll(ballot64(r.k[e] >= x));
+      }
     }
+  if constexpr (SPL >= 64) c = wave_sum_int(c);
   return c;
 }
 
