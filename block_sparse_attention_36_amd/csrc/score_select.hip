@@ -103,6 +103,7 @@ struct SelArgs {
   unsigned long long* mask;
   int* counts;
   int nb, nw, rows, G, per_group;
+  int units, i0, ni;  // register form: this launch's query blocks [i0, i0 + ni) of every unit
   int top_k, force_sink, gate, gate_factor;
   float gate_threshold, tau_log2e, mass_threshold;
   double rescue_fraction;
@@ -465,10 +466,11 @@ __global__ __launch_bounds__(256) void select_reg_kernel(SelArgs a) {
   const int l = lane_id();
   // (the wave index through readfirstlane: row, i and the slot count are then
   // known to be wave-uniform, and the per-slot conditions below scalar branches)
-  const int row = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (row >= a.rows) return;  // no workgroup barriers below
+  const int r = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nb = a.nb;
-  const int u = row / nb, i = row % nb;
+  if (r >= a.units * a.ni) return;  // no workgroup barriers below
+  const int u = r / a.ni, i = a.i0 + r % a.ni;
+  const int row = u * nb + i;
   const int g = a.per_group ? u : u / a.G;
   const int sink = a.force_sink;
   const int nc = i > 0 ? i - (sink ? 1 : 0) : 0;
@@ -950,6 +952,9 @@ hipError_t launch_score_select(const Shape& sh, const SelectConfig& cfg, const f
   a.nb = nb;
   a.nw = nw;
   a.rows = rows;
+  a.units = nb > 0 ? rows / nb : 0;
+  a.i0 = 0;
+  a.ni = nb;
   a.G = sh.G();
   a.per_group = sh.per_group;
   a.top_k = cfg.top_k;
@@ -967,35 +972,57 @@ hipError_t launch_score_select(const Shape& sh, const SelectConfig& cfg, const f
   a.mask_x = sig ? (unsigned long long*)(ws + w.mask_x_off) : nullptr;
   a.counts_x = sig ? (int*)(ws + w.counts_x_off) : nullptr;
   // register form for rows up to 64*SPL = 4096 blocks (8192 with the top-k and
-  // gate branches only), LDS form beyond
+  // gate branches only), LDS form beyond.  When rows reach 64 slots the register
+  // form runs once per range of query blocks [64*SPL/2, 64*SPL), each with the
+  // fewest slots its rows need (rows below 1024 blocks share the 16-slot launch),
+  // longest rows first; with the top-k and gate branches only, the 32- to 128-slot
+  // forms leave out the rescue and mass state.
   const bool topk_only = !a.use_b && !a.use_p;
   const int spl = nw <= 1 ? 1 : nw <= 2 ? 2 : nw <= 4 ? 4 : nw <= 8 ? 8 : nw <= 16 ? 16
                   : nw <= 32 ? 32 : nw <= 64 ? 64 : (nw <= 128 && topk_only) ? 128 : 0;
-  const dim3 rg((rows + 3) / 4), rb(256);
-#define BSA_SELECT_REG(N, F)                                                               \
-  case N:                                                                                  \
-    if (sig)                                                                               \
-      hipLaunchKernelGGL((select_reg_kernel<N, F, true>), rg, rb, 0, stream, a);           \
-    else                                                                                   \
-      hipLaunchKernelGGL((select_reg_kernel<N, F, false>), rg, rb, 0, stream, a);          \
-    break;
-  switch (spl) {
-    BSA_SELECT_REG(1, true)
-    BSA_SELECT_REG(2, true)
-    BSA_SELECT_REG(4, true)
-    BSA_SELECT_REG(8, true)
-    BSA_SELECT_REG(16, true)
-    BSA_SELECT_REG(32, true)
-    BSA_SELECT_REG(64, true)
-    BSA_SELECT_REG(128, false)
+// one launch of the register form: N slots, FULL (every branch) or top-k only,
+// the sigma gate's form when it is on
+#define BSA_SELECT_REG(N, F)                                                          \
+  if (sig)                                                                            \
+    hipLaunchKernelGGL((select_reg_kernel<N, F, true>), rg, rb, 0, stream, a);        \
+  else                                                                                \
+    hipLaunchKernelGGL((select_reg_kernel<N, F, false>), rg, rb, 0, stream, a);       \
+  break;
+  if (spl > 0) {
+    // (short layers, widest form below 64 slots: a single launch)
+    const int smin = spl >= 64 ? 16 : spl;
+    for (int s = spl; s >= smin; s /= 2) {
+      const int lo = (s == smin) ? 0 : 64 * s / 2;
+      const int hi = 64 * s < nb ? 64 * s : nb;
+      if (lo >= hi) continue;
+      a.i0 = lo;
+      a.ni = hi - lo;
+      const dim3 rg((unsigned)(((int64_t)a.units * a.ni + 3) / 4)), rb(256);
+      const int form = (topk_only && s >= 32) ? -s : s;  // negative: top-k-only form
+      switch (form) {
+        case 1: BSA_SELECT_REG(1, true)
+        case 2: BSA_SELECT_REG(2, true)
+        case 4: BSA_SELECT_REG(4, true)
+        case 8: BSA_SELECT_REG(8, true)
+        case 16: BSA_SELECT_REG(16, true)
+        case 32: BSA_SELECT_REG(32, true)
+        case 64: BSA_SELECT_REG(64, true)
+        case -32: BSA_SELECT_REG(32, false)
+        case -64: BSA_SELECT_REG(64, false)
+        case -128: BSA_SELECT_REG(128, false)
+        default:
+          return hipErrorInvalidValue;
+      }
 #undef BSA_SELECT_REG
-    default: {
-      const size_t per_wave_bytes = (size_t)a.per_wave_floats * sizeof(float);
-      int waves = (int)(65536 / per_wave_bytes);
-      waves = waves < 1 ? 1 : (waves > 4 ? 4 : waves);
-      hipLaunchKernelGGL(select_kernel, dim3((rows + waves - 1) / waves), dim3(64 * waves),
-                         waves * per_wave_bytes, stream, a);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
     }
+  } else {
+    const size_t per_wave_bytes = (size_t)a.per_wave_floats * sizeof(float);
+    int waves = (int)(65536 / per_wave_bytes);
+    waves = waves < 1 ? 1 : (waves > 4 ? 4 : waves);
+    hipLaunchKernelGGL(select_kernel, dim3((rows + waves - 1) / waves), dim3(64 * waves),
+                       waves * per_wave_bytes, stream, a);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
