@@ -160,6 +160,9 @@ def test_padded_list_matches_csr(cfg):
 MID = [scaled(config_by_name("msa1m"), 2000 * 128 + 17, num_q_heads=4, num_kv_heads=2),
        scaled(config_by_name("dual128k"), 4000 * 128 - 3, num_q_heads=2, num_kv_heads=1),
        scaled(config_by_name("gated64k"), 3000 * 128, num_q_heads=2, num_kv_heads=1),
+       # rows past 64 register slots: the register form runs once per range of query
+       # blocks, and here the widest range holds the last query block alone
+       scaled(config_by_name("gated64k"), 4096 * 128 + 5, num_q_heads=2, num_kv_heads=1),
        # the sigma gate in the 128-slot register form and, past 8192 blocks, in the
        # LDS form with the tile keys in global memory
        scaled(config_by_name("sigma64k"), 6000 * 128, num_q_heads=2, num_kv_heads=1),
