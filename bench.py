@@ -241,12 +241,23 @@ def _pmc_rows(d: str, counter: str):
 ATTN_KERNEL = "attn_whole_kernel"
 
 
+# How the counter record is made (run from /tmp with TMPDIR=/tmp; $R is the repository).
+PMC_COMMANDS = [
+    "rocprofv3 --pmc {c} --kernel-include-regex \"attn_|pool_|select_|score_|copy|scan_|compact_\" "
+    "--output-format csv -d $R/gpurun_out/pmc_{d} -o run -- python3 $R/bench.py --steps 1 --warmup 1 "
+    "--no-cpu-baseline --calibrate-copy".format(c=c, d=d)
+    for c, d in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write"))
+] + ["python3 $R/bench.py --summarize-pmc $R/gpurun_out/pmc_fetch $R/gpurun_out/pmc_write "
+     "$R/profiles/attention_dual128k_counters.json"]
+
+
 def summarize_pmc(fetch_dir: str, write_dir: str, out_json: str) -> int:
     """HBM bytes per attention launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
     each scaled by what the same counter reads for a plain copy of COPY_BYTES."""
     import statistics
     out = {"kernel": "attn_whole_kernel<128, 128, false>", "workload": "dual128k",
-           "kernel_source_hash": source_hash("attention.hip", "common.h")}
+           "kernel_source_hash": source_hash("attention.hip", "common.h"),
+           "commands": PMC_COMMANDS}
     others = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = _pmc_rows(d, counter)
