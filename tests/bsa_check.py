@@ -265,7 +265,8 @@ def _check_pool_and_scores(cfg, host, run, blocks, rng, score_sample):
             bound = 1e-4 * np.linalg.norm(qbar[u, 0]) * np.linalg.norm(kbar[0, 0])
             assert abs(sg - sref) <= bound + 1e-30, f"score ({u},{i},{j}): {sg} vs {sref}"
             if b_gpu is not None:
-                bref = sref + qnorm[u, 0] * rad[0, 0]
+                bref = float(O.rescue_bounds(np.array([[[sref]]]), qnorm[u:u + 1, :1],
+                                             rad[:1, :1], 1, 1, "qhead")[0, 0, 0])
                 bb = 1e-4 * np.linalg.norm(qbar[u, 0]) * (np.linalg.norm(kbar[0, 0]) + rad[0, 0])
                 assert abs(float(b_gpu[u, i, j]) - bref) <= bb + 1e-30, f"bound ({u},{i},{j})"
 

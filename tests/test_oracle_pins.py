@@ -134,30 +134,77 @@ def test_scores_bilinear_identity_against_dense_logits():
 
 
 def test_rescue_bound_cauchy_schwarz_invariant():
+    # GQA shape (4 query heads per kv head): each unit's bound must use its own
+    # kv head's keys and radius
     rng = np.random.default_rng(7)
-    S, Hq, Hkv, D, B = 64, 2, 1, 8, 8
+    S, Hq, Hkv, D, B = 64, 8, 2, 8, 8
+    G = Hq // Hkv
     Q = rng.standard_normal((S, Hq, D))
-    K = rng.standard_normal((S, Hkv, D)) * rng.uniform(0.1, 3.0, size=(S, 1, 1))
+    K = rng.standard_normal((S, Hkv, D)) * rng.uniform(0.1, 3.0, size=(S, Hkv, 1))
     qbar, qn = O.pool_queries(Q, B, Hkv, "qhead")
     kbar, r = O.pool_keys(K, B)
     s = O.block_scores(qbar, kbar, Hq, Hkv, "qhead")
     b = O.rescue_bounds(s, qn, r, Hq, Hkv, "qhead")
     nb = S // B
-    tight = 0
     for u in range(Hq):
+        g = u // G
         for i in range(nb):
             for j in range(i + 1):
-                best_key = (K[j * B:(j + 1) * B, 0] @ qbar[u, i]).max()
+                best_key = (K[j * B:(j + 1) * B, g] @ qbar[u, i]).max()
                 assert b[u, i, j] >= best_key - 1e-12
                 assert b[u, i, j] >= s[u, i, j]
-                tight += b[u, i, j] - best_key < 1e-9
     # equality when the block's keys are identical (radius 0)
-    K2 = np.repeat(rng.standard_normal((nb, 1, D)), B, axis=0)
+    K2 = np.repeat(rng.standard_normal((nb, Hkv, D)), B, axis=0)
     kbar2, r2 = O.pool_keys(K2, B)
     s2 = O.block_scores(qbar, kbar2, Hq, Hkv, "qhead")
     b2 = O.rescue_bounds(s2, qn, r2, Hq, Hkv, "qhead")
     m = ~np.isnan(s2)
     assert np.allclose(b2[m], s2[m], atol=1e-12)
+
+
+def test_rescue_bound_closed_form_and_tight_on_aligned_blocks():
+    """Closed form, from the construction alone: every query row of head h is the
+    same vector w_h, so qbar[h, i] = w_h for all i; block j of kv head g holds
+    keys c_gj + a_gj*e and c_gj - a_gj*e (e a unit vector), so its centroid is
+    c_gj and its radius a_gj.  Hence b[h, i, j] = w_h.c_gj + ||w_h||*a_gj exactly,
+    with g = h // 4.  For the head whose w points along its kv head's e, the
+    bound is attained by the key c + a*e: b equals the best key's dot product.
+    The radii differ per kv head, so a bound built from another kv head's
+    radius, or with 2*||qbar||*r, misses the closed form."""
+    rng = np.random.default_rng(71)
+    S, Hq, Hkv, D, B = 48, 8, 2, 6, 8
+    G = Hq // Hkv
+    nb = S // B
+    e = rng.standard_normal((Hkv, D))
+    e /= np.linalg.norm(e, axis=1, keepdims=True)
+    w = rng.standard_normal((Hq, D))
+    aligned = [g * G + 1 for g in range(Hkv)]  # head 1 of each group looks along e_g
+    for g, h in enumerate(aligned):
+        w[h] = 2.5 * e[g]
+    c = rng.standard_normal((Hkv, nb, D))
+    a = np.stack([rng.uniform(0.5, 1.0, nb), rng.uniform(2.0, 4.0, nb)])  # [Hkv, nb]
+    Q = np.broadcast_to(w[None], (S, Hq, D)).copy()
+    K = np.zeros((S, Hkv, D))
+    for g in range(Hkv):
+        for j in range(nb):
+            for t in range(B):
+                sign = 1.0 if t % 2 == 0 else -1.0
+                K[j * B + t, g] = c[g, j] + sign * a[g, j] * e[g]
+    qbar, qn = O.pool_queries(Q, B, Hkv, "qhead")
+    kbar, r = O.pool_keys(K, B)
+    s = O.block_scores(qbar, kbar, Hq, Hkv, "qhead")
+    b = O.rescue_bounds(s, qn, r, Hq, Hkv, "qhead")
+    for h in range(Hq):
+        g = h // G
+        for i in range(nb):
+            for j in range(i + 1):
+                expect = w[h] @ c[g, j] + np.linalg.norm(w[h]) * a[g, j]
+                assert abs(b[h, i, j] - expect) < 1e-10, (h, i, j)
+                best_key = (K[j * B:(j + 1) * B, g] @ w[h]).max()
+                if h in aligned:
+                    assert abs(b[h, i, j] - best_key) < 1e-10, (h, i, j)
+                else:
+                    assert b[h, i, j] > best_key + 1e-6, (h, i, j)
 
 
 # ---------------------------------------------------------------- Quest backbone
@@ -569,6 +616,57 @@ def test_acceptable_sets_cover_near_threshold():
     assert amb and len(sets) == 2
     sets, amb = O.acceptable_row_sets(2, np.array([0.0, 3.0, 0.0]), None, p, 1e-5)
     assert not amb and len(sets) == 1
+
+
+def _mass_row(cum_targets):
+    """Scores whose softmax (temperature 1) over candidates 0..n-1 has the given
+    cumulative sums (candidate j has the j-th largest probability); the row's
+    last entry is its forced diagonal block."""
+    cum = np.asarray(cum_targets, dtype=np.float64)
+    p = np.diff(np.concatenate([[0.0], cum]))
+    assert np.all(p > 0) and np.all(np.diff(p) <= 0) and abs(cum[-1] - 1.0) < 1e-15
+    return np.concatenate([np.log(p), [0.0]])
+
+
+@pytest.mark.parametrize("mu,cum,accepted", [
+    # cumulative mass of the first 3 candidates just above mu, within delta:
+    # stopping at 3 (float64 decision) or at 4 (a float32 sum a hair low)
+    (0.9, [0.5, 0.8, 0.9 + 5e-6, 0.95, 0.98, 1.0], [3, 4]),
+    # just below mu, within delta: 4 in float64, 3 if a float32 sum is a hair high
+    (0.9, [0.5, 0.8, 0.9 - 5e-6, 0.95, 0.98, 1.0], [3, 4]),
+    # outside the band on either side: only the float64 decision
+    (0.9, [0.5, 0.8, 0.9 + 2e-5, 0.95, 0.98, 1.0], [3]),
+    (0.9, [0.5, 0.8, 0.9 - 2e-5, 0.95, 0.98, 1.0], [4]),
+    # every prefix short of the whole row stays below mu - delta: all of them
+    (0.9, [0.3, 0.5, 0.65, 0.78, 0.9 - 2e-5, 1.0], [6]),
+    # the whole row is reachable when the prefix before it sits inside the band
+    (0.9, [0.3, 0.5, 0.65, 0.78, 0.9 - 5e-6, 1.0], [5, 6]),
+    # two consecutive prefix masses inside the band (mu close to 1, so that the
+    # tail after the band can hold candidates no larger than the one inside it):
+    # three lengths reachable
+    (0.99998, [0.6, 0.9, 0.99998 - 5e-6, 0.99998 + 4e-6, 0.999992, 1.0], [3, 4, 5]),
+])
+def test_acceptable_sets_mass_branch_hand_cases(mu, cum, accepted):
+    """The base branch's accepted prefix lengths near mu with delta = 1e-5, worked
+    out by hand: a prefix length m is reachable when its own mass is within delta
+    of reaching mu (or it is the whole row) and the mass before it is within
+    delta of not reaching mu."""
+    delta = 1e-5
+    n = len(cum)
+    i = n  # candidates 0..n-1, forced diagonal n
+    s = _mass_row(cum)
+    p = O.SelectParams(mass_threshold=mu)
+    sets, amb = O.acceptable_row_sets(i, s, None, p, delta)
+    lengths = sorted(len(kept) - 1 for kept, _ in sets)
+    assert lengths == accepted
+    for kept, fired in sets:
+        m = len(kept) - 1
+        assert kept == list(range(m)) + [i] and not fired
+    assert amb == (len(accepted) > 1)
+    # the plain decision is one of them
+    kept, _ = O.select_row(i, s, None, p)
+    assert len(kept) - 1 in accepted
+
 
 
 # ---------------------------------------------------------------- attention
