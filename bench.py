@@ -182,7 +182,9 @@ def cpu_baseline(cfg, inp, sel_rows, budget_s: float = 15.0):
         kbar, rad = O.pool_keys(K, B)
     flops = 0.0
     units = 0
+    ambiguous = 0
     heads = [h for h in range(Hq) if h // G == kv]
+    c0 = time.process_time()
     while time.perf_counter() - t0 < budget_s:
         i = int(rng.integers(nb))
         h = heads[int(rng.integers(len(heads)))]
@@ -201,6 +203,7 @@ def cpu_baseline(cfg, inp, sel_rows, budget_s: float = 15.0):
         if p.gate == "sigma_cut":
             O.sigma_cut_margin(s, O.candidate_sets(i, p.force_sink)[1], p.top_k)
         kept, _ = O.select_row(i, s, b, p)
+        ambiguous += int(O.acceptable_row_sets(i, s, b, p, 1e-5)[1])
         keys = O.block_tokens(kept, B, S)
         O.attend(qh[:, h], i * B + np.arange(qh.shape[0]), K[keys, 0], V[keys, 0], keys,
                  1 / math.sqrt(D))
@@ -210,12 +213,8 @@ def cpu_baseline(cfg, inp, sel_rows, budget_s: float = 15.0):
             flops += 4 * D * (nq * (nq + 1) // 2 if j == i else nq * nk)
         units += 1
     el = time.perf_counter() - t0
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([x.get("num_threads", 1) for x in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover - threadpoolctl missing
-        cores = len(os.sched_getaffinity(0))
-    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+    cpu = time.process_time() - c0
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "kind": "oracle",
             "sample": (f"{units} random (query block, head) rows of kv head 0 at S={S}: "
                        + ("Quest row bounds vs all key blocks" if quest
                           else "pool + score vs all key blocks")
@@ -225,7 +224,159 @@ def cpu_baseline(cfg, inp, sel_rows, budget_s: float = 15.0):
                        + f" + attention, plus {'bounds' if quest else 'pooling'} of "
                        f"kv head 0's {nb} key blocks, {el:.1f} s of float64 NumPy "
                        f"(host copy {copy_s:.1f} s excluded)"),
-            "seconds": round(el, 2)}
+            "seconds": round(el, 2), "rows": units,
+            "ambiguous_rows": ambiguous, **_cpu_fields(el, cpu)}
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _cpu_fields(wall_s: float, cpu_s: float) -> dict:
+    """Core accounting of an oracle run: the process's CPU time over its wall time is
+    the number of cores it kept busy on average (NumPy's BLAS calls are threaded,
+    the row loop is not); the affinity set and the BLAS thread count are the
+    ceiling it had."""
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([x.get("num_threads", 1) for x in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        blas = None
+    return {"cores": max(1, int(round(cpu_s / wall_s))) if wall_s > 0 else 1,
+            "cores_busy_avg": round(cpu_s / wall_s, 2) if wall_s > 0 else None,
+            "affinity_cores": len(os.sched_getaffinity(0)), "blas_threads": blas,
+            "cpu_model": _cpu_model()}
+
+
+def cpu_full(cfg, inp):
+    """The CPU oracle over the whole workload (every pool entry, score, row and
+    attention output), timed: for the workloads small enough to finish in
+    minutes.  Host copies and the decoding of the stored bytes are excluded."""
+    import numpy as np
+    import torch
+    from oracle import bsa_oracle as O
+    B, D = cfg.block_size, cfg.head_dim
+    Hq, Hkv, gran = cfg.num_q_heads, cfg.num_kv_heads, cfg.granularity
+    p = O.SelectParams(cfg.top_k, cfg.force_sink, cfg.gate, cfg.gate_threshold, cfg.gate_factor,
+                       cfg.score_temperature, cfg.mass_threshold,
+                       cfg.rescue_fraction).as_library_precision()
+    fp8 = cfg.dtype == "fp8"
+
+    def host(t, sc):
+        t = t.cpu()
+        raw = t.numpy() if fp8 else t.view(torch.int16).numpy().view(np.uint16)
+        return O.dequantize(raw, sc.cpu().numpy().astype(np.float64), B) if fp8 \
+            else O.decode_bf16(raw)
+
+    Q, K, V = host(inp.q, inp.q_scale), host(inp.k, inp.k_scale), host(inp.v, inp.v_scale)
+    t0, c0 = time.perf_counter(), time.process_time()
+    b = None
+    if cfg.backbone == "quest":
+        kmin, kmax = O.key_block_bounds(K, B)
+        s = O.quest_scores(Q, kmin, kmax, B, Hkv, gran)
+    else:
+        qbar, qn = O.pool_queries(Q, B, Hkv, gran)
+        kbar, rad = O.pool_keys(K, B)
+        s = O.block_scores(qbar, kbar, Hq, Hkv, gran)
+        if p.rescue_fraction > 0:
+            b = O.rescue_bounds(s, qn, rad, Hq, Hkv, gran)
+    kept, _ = O.select(s, b, p)
+    print(f"[bench] oracle: pool, scores and selection done ({time.perf_counter() - t0:.1f} s)",
+          file=sys.stderr, flush=True)
+    for h in range(Hq):
+        O.attention(Q, K, V, kept, B, 1 / math.sqrt(D), gran, heads=[h])
+        if (h + 1) % 4 == 0 or h + 1 == Hq:
+            print(f"[bench] oracle: attention of {h + 1}/{Hq} heads "
+                  f"({time.perf_counter() - t0:.1f} s)", file=sys.stderr, flush=True)
+    el, cpu = time.perf_counter() - t0, time.process_time() - c0
+    rp, ci = O.to_csr(kept)
+    flops = attention_flops(rp, ci, cfg)
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "kind": "oracle",
+            "sample": f"the whole workload: {cfg.num_units * cfg.num_blocks} selection rows, "
+                      f"{Hq * cfg.num_blocks} attention units, {el:.1f} s of float64 NumPy",
+            "seconds": round(el, 2), **_cpu_fields(el, cpu)}
+
+
+def realized_stats(cfg, meta, rp, ci, gate):
+    """What the synthetic structure did under the selection (reported, never
+    tuned): recall of the planted needle blocks, of the planted pairs and of the
+    wide blocks' outlier keys, and the gate's firing rate on rows with a planted
+    near tie against the other rows."""
+    import numpy as np
+    nb, U, G = cfg.num_blocks, cfg.num_units, cfg.group_size
+    kept = {}
+
+    def row(u, i):
+        r = u * nb + i
+        if r not in kept:
+            kept[r] = set(int(x) for x in ci[rp[r]:rp[r + 1]])
+        return kept[r]
+
+    kv_of = (lambda u: u // G) if cfg.granularity == "qhead" else (lambda u: u)
+    out = {}
+    needles = meta.get("needle_blocks") or []
+    if needles:
+        hit = tot = 0
+        for u in range(U):
+            for i in range(nb):
+                elig = [n for n in needles if n < i and not (cfg.force_sink and n == 0)]
+                if elig:
+                    r = row(u, i)
+                    hit += sum(n in r for n in elig)
+                    tot += len(elig)
+        out["needle_recall"] = round(hit / tot, 4) if tot else None
+        out["needle_pairs"] = tot
+    planted = meta.get("planted_query_blocks") or {}
+    pairs = meta.get("pairs") or {}
+    if planted:
+        both = needle = tot = 0
+        fire_p = n_p = fire_b = n_b = 0
+        for u in range(U):
+            g = kv_of(u)
+            pl = planted.get(g, {})
+            for i in range(nb):
+                if i in pl:
+                    a, b_ = pairs[g][pl[i]]
+                    r = row(u, i)
+                    needle += a in r
+                    both += (a in r) and (b_ in r)
+                    tot += 1
+                if gate is not None:
+                    f = bool(gate[u * nb + i])
+                    if i in pl:
+                        fire_p += f
+                        n_p += 1
+                    else:
+                        fire_b += f
+                        n_b += 1
+        out["planted_rows"] = tot
+        out["planted_needle_recall"] = round(needle / tot, 4) if tot else None
+        out["planted_pair_recall"] = round(both / tot, 4) if tot else None
+        if gate is not None and cfg.gate != "none":
+            out["gate_fire_rate_planted"] = round(fire_p / n_p, 4) if n_p else None
+            out["gate_fire_rate_background"] = round(fire_b / n_b, 4) if n_b else None
+    wide = meta.get("wide_blocks") or {}
+    if wide:
+        hit = tot = 0
+        for g, outl in wide.items():
+            for b_, (_, later, hsel) in outl.items():
+                if later <= b_:
+                    continue
+                u = hsel if cfg.granularity == "qhead" else g
+                hit += b_ in row(u, later)
+                tot += 1
+        out["outlier_block_recall"] = round(hit / tot, 4) if tot else None
+        out["outlier_rows"] = tot
+    if gate is not None:
+        out["gate_fire_rate"] = round(float(np.mean(gate)), 4)
+    return out
 
 
 COPY_BYTES = 1 << 30
@@ -338,6 +489,9 @@ def main(argv=None) -> int:
     ap.add_argument("--index-format", choices=("csr", "padded"), default="csr",
                     help="kept-block lists as CSR, or as the uniform sentinel-padded list")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-full", action="store_true",
+                    help="time the CPU oracle on the whole workload instead of a sample "
+                         "(minutes for tiny, gqa32k and gated64k; not for the larger ones)")
     ap.add_argument("--dense-context", action="store_true",
                     help="after timing, run the same attention kernel on the full causal mask "
                          "(dense prefill, context: speedup of the sparse step over it)")
@@ -398,6 +552,8 @@ def main(argv=None) -> int:
     lse = torch.empty(cfg.num_q_heads, cfg.seq_len, dtype=torch.float32, device=dev)
     scale = 1.0 / math.sqrt(cfg.head_dim)
 
+    sc_last = [None]
+
     def step(ev=None):
         if ev:
             ev[0].record()
@@ -410,6 +566,7 @@ def main(argv=None) -> int:
         sc = None
         if quest:
             sc = bsa.bsa_quest_scores(problem, inp.q, kb[0], kb[1], inp.q_scale, buffers=qbufs)
+            sc_last[0] = sc
             if ev:
                 ev[4].record()
         if padded:
@@ -525,6 +682,18 @@ def main(argv=None) -> int:
         "gb": round(pb / 1e9, 4), "gbs": round(pb / (float(pool_ms.mean()) * 1e-3) / 1e9, 1),
         "frac_hbm": round(pb / (float(pool_ms.mean()) * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "frac_copy": round(pb / (float(pool_ms.mean()) * 1e-3) / 1e9 / copy_gbs, 4)}
+    gate = None
+    if cfg.gate != "none" and not padded:
+        if quest:
+            xs = bsa.bsa_select_scores(problem, params, sc_last[0], export=True)
+        else:
+            xs = bsa.bsa_score_select(problem, params, pool, export=True)
+        torch.cuda.synchronize()
+        gate = xs.gate.cpu().numpy()
+        del xs
+        torch.cuda.empty_cache()
+    res["realized"] = realized_stats(cfg, inp.meta, rp, ci, gate)
+    res["realized"]["density"] = res["density"]
     if args.calibrate_copy:
         src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
@@ -536,7 +705,10 @@ def main(argv=None) -> int:
         print("[bench] dense causal attention (context)", file=sys.stderr, flush=True)
         res["dense_context"] = dense_context(bsa, torch, problem, cfg, inp, scale, out, lse,
                                              attn_avg, ms_per_step)
-    if not args.no_cpu_baseline:
+    if args.cpu_full:
+        print("[bench] cpu baseline (oracle, whole workload)", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_full(cfg, inp)
+    elif not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(cfg, inp, None, args.cpu_seconds)
     else:

@@ -87,6 +87,7 @@ def load_library(path: str = LIB_PATH):
         "bsa_select_scores_workspace_size": ([PP, PS], SZ),
         "bsa_select_scores": ([PP, PS, P, P, P, I64, P, P, SZ, P], ctypes.c_int),
         "bsa_padded_width": ([PP, PS], I64),
+        "bsa_select_overflow_offset": ([PP, PS, ctypes.c_int], I64),
         "bsa_score_select_padded_workspace_size": ([PP, PS, ctypes.c_int], SZ),
         "bsa_score_select_padded": ([PP, PS, P, P, P, P, P, P, I64, P, P, P, P, SZ, P],
                                     ctypes.c_int),
@@ -152,6 +153,25 @@ class Selection:
     scores: object = None
     bounds: object = None
     gate: object = None
+    buffers: object = None
+
+    def overflowed(self) -> bool:
+        """Whether the call reported a kept set too large for its output (reads the
+        workspace word back, so it synchronises with the device)."""
+        return self.buffers.overflowed()
+
+
+def _overflow_offset(problem, params, scores_given_or_exported) -> int:
+    L = load_library()
+    off = L.bsa_select_overflow_offset(ctypes.byref(problem), ctypes.byref(params),
+                                       int(scores_given_or_exported))
+    if off < 0:
+        raise BsaError(1, load_library().bsa_last_error().decode())
+    return int(off)
+
+
+def _read_overflow(workspace, offset: int) -> bool:
+    return bool(workspace[offset:offset + 4].view(__import__("torch").int32).item())
 
 
 def _u8(t):
@@ -204,6 +224,7 @@ class SelectBuffers:
         self.col_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=device)
         self.capacity = cap
         self.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=device)
+        self.overflow_offset = _overflow_offset(problem, params, export or given_scores)
         self.scores = self.bounds = self.gate = None
         if export:
             if not given_scores:
@@ -211,6 +232,9 @@ class SelectBuffers:
                 if params.rescue_fraction > 0:
                     self.bounds = torch.empty(U, nb, nb, dtype=torch.float32, device=device)
             self.gate = torch.empty(rows, dtype=torch.uint8, device=device)
+
+    def overflowed(self) -> bool:
+        return _read_overflow(self.workspace, self.overflow_offset)
 
 
 def bsa_score_select(problem: Problem, params: SelectParams, pool: PoolResult, export=False,
@@ -223,7 +247,7 @@ def bsa_score_select(problem: Problem, params: SelectParams, pool: PoolResult, e
                               _ptr(b.row_ptr), _ptr(b.col_idx), b.capacity, _ptr(b.scores),
                               _ptr(b.bounds), _ptr(b.gate), _ptr(b.workspace),
                               b.workspace.numel(), _stream(dev)))
-    return Selection(b.row_ptr, b.col_idx, None, b.scores, b.bounds, b.gate)
+    return Selection(b.row_ptr, b.col_idx, None, b.scores, b.bounds, b.gate, b)
 
 
 def bsa_pool_key_bounds(problem: Problem, k, k_scale=None, out=None):
@@ -279,7 +303,7 @@ def bsa_select_scores(problem: Problem, params: SelectParams, scores, export=Fal
     _check(L.bsa_select_scores(ctypes.byref(problem), ctypes.byref(params), _ptr(scores),
                                _ptr(b.row_ptr), _ptr(b.col_idx), b.capacity, _ptr(b.gate),
                                _ptr(b.workspace), b.workspace.numel(), _stream(dev)))
-    return Selection(b.row_ptr, b.col_idx, None, scores if export else None, None, b.gate)
+    return Selection(b.row_ptr, b.col_idx, None, scores if export else None, None, b.gate, b)
 
 
 class PaddedBuffers:
@@ -302,6 +326,7 @@ class PaddedBuffers:
         self.width = max(int(width), 1)
         self.kv_idx = torch.empty(rows, self.width, dtype=torch.int32, device=device)
         self.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=device)
+        self.overflow_offset = _overflow_offset(problem, params, export or given_scores)
         self.scores = self.bounds = self.gate = None
         if export:
             if not given_scores:
@@ -309,6 +334,9 @@ class PaddedBuffers:
                 if params.rescue_fraction > 0:
                     self.bounds = torch.empty(U, nb, nb, dtype=torch.float32, device=device)
             self.gate = torch.empty(rows, dtype=torch.uint8, device=device)
+
+    def overflowed(self) -> bool:
+        return _read_overflow(self.workspace, self.overflow_offset)
 
 
 def bsa_score_select_padded(problem: Problem, params: SelectParams, pool: PoolResult | None = None,

@@ -152,6 +152,18 @@ bsa::SelectConfig select_config(const bsa_select_params* params) {
   return cfg;
 }
 
+// Rows too long for the register form of the select kernel keep each row in LDS
+// (scores, plus bounds and probabilities when the rescue and mass branches are
+// on); rows needing more than one CU's LDS are not supported.
+bsa_status check_select_form(const bsa::Shape& sh, const bsa_select_params* params) {
+  const size_t need = bsa::select_lds_bytes(sh, select_config(params));
+  if (need > bsa::select_lds_limit())
+    return fail(BSA_ERR_UNSUPPORTED,
+                "rows of %d blocks need %zu bytes of LDS per selection row with these branches "
+                "(at most %zu)", sh.nb, need, bsa::select_lds_limit());
+  return BSA_OK;
+}
+
 bool misaligned(const void* p) { return ((uintptr_t)p & 15) != 0; }
 
 bsa_status device_status(hipError_t e, const char* what) {
@@ -235,6 +247,8 @@ bsa_status bsa_score_select(const bsa_problem* problem, const bsa_select_params*
   bsa_status st = check_problem(problem, sh);
   if (st != BSA_OK) return st;
   st = check_params(params);
+  if (st != BSA_OK) return st;
+  st = check_select_form(sh, params);
   if (st != BSA_OK) return st;
   if (sh.S == 0) return ok();
   if (!q_centroid || !k_centroid || !row_ptr || !col_idx)
@@ -322,6 +336,8 @@ bsa_status bsa_select_scores(const bsa_problem* problem, const bsa_select_params
   if (st != BSA_OK) return st;
   st = check_params(params);
   if (st != BSA_OK) return st;
+  st = check_select_form(sh, params);
+  if (st != BSA_OK) return st;
   if (params->rescue_fraction > 0.0)
     return fail(BSA_ERR_INVALID_ARGUMENT,
                 "the rescue branch needs centroid scores and radii (use bsa_score_select)");
@@ -346,6 +362,15 @@ bsa_status bsa_select_scores(const bsa_problem* problem, const bsa_select_params
                                col_capacity, nullptr, nullptr, gate_out, workspace,
                                (hipStream_t)hip_stream, scores),
       "bsa_select_scores launch");
+}
+
+int64_t bsa_select_overflow_offset(const bsa_problem* problem, const bsa_select_params* params,
+                                   int scores_given_or_exported) {
+  bsa::Shape sh;
+  if (check_problem(problem, sh) != BSA_OK || check_params(params) != BSA_OK) return -1;
+  return (int64_t)bsa::select_workspace_layout(sh, scores_given_or_exported != 0,
+                                               params->gate == BSA_GATE_SIGMA_CUT)
+      .overflow_off;
 }
 
 int64_t bsa_padded_width(const bsa_problem* problem, const bsa_select_params* params) {
@@ -374,6 +399,8 @@ bsa_status bsa_score_select_padded(const bsa_problem* problem, const bsa_select_
   bsa_status st = check_problem(problem, sh);
   if (st != BSA_OK) return st;
   st = check_params(params);
+  if (st != BSA_OK) return st;
+  st = check_select_form(sh, params);
   if (st != BSA_OK) return st;
   const bool rescue = params->rescue_fraction > 0.0;
   if (scores_in && (rescue || scores_out || bound_out))

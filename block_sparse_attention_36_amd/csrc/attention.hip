@@ -435,7 +435,10 @@ __global__ __launch_bounds__(64 * (B / 32), 2) void attn_whole_kernel(AttnArgs a
     // for the issue slots first; for the next block's request and products it
     // yields, so a wave in its softmax runs ahead of one in its products.
     __builtin_amdgcn_s_setprio(2);
-    const float sl = a.scale_log2 * qsc * ksc;
+    // (an all-zero E4M3 block has scale 0: its logits are all zero, and a floor
+    // of 1e-30 on the logit scale keeps them so, to within 1e-22, while masked
+    // keys stay at -inf instead of becoming -inf * 0 = NaN)
+    const float sl = fmaxf(a.scale_log2 * qsc * ksc, 1e-30f);
     float mx = -INFINITY;
     if (j < 0 || j == i || (int64_t)j * B + B > a.S) {
       int lim = -1;

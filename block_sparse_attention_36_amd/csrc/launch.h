@@ -28,11 +28,17 @@ struct SelectConfig {
 
 // Workspace carve-up used by launch_score_select (byte offsets, 256-aligned).
 struct SelectWorkspace {
-  size_t scores_off, mask_off, counts_off;
+  size_t scores_off, mask_off, counts_off, overflow_off;
   size_t sigma_off, mask_x_off, counts_x_off, keys_off, fire_off;  // sigma gate only
   size_t total;
 };
 SelectWorkspace select_workspace_layout(const Shape& sh, bool export_scores, bool sigma_gate);
+
+// Dynamic LDS the select kernel's LDS form needs for these rows (0 when the
+// register form runs), and the most one workgroup may have; above the limit the
+// selection is not supported.
+size_t select_lds_bytes(const Shape& sh, const SelectConfig& cfg);
+size_t select_lds_limit();
 
 // scores_in != nullptr: selection on the given scores [U, nb, nb] (no centroid
 // scores are computed; q_centroid and k_centroid are unused).  width > 0: the

@@ -30,6 +30,8 @@
 //
 // CSR: a single-workgroup exclusive scan of the row counts, then one wave per row
 // writes the set bits of its mask in ascending order.
+#include <atomic>
+
 #include "common.h"
 #include "launch.h"
 
@@ -113,7 +115,16 @@ struct SelArgs {
   float* sigma;
   unsigned long long* mask_x;
   int* counts_x;
+  // set to 1 when some row's kept set does not fit the output (cleared here,
+  // written by the scan or, for the padded list, by compaction)
+  int* overflow;
 };
+
+// Clears the overflow word once per launch (every launch of a selection comes
+// before its compaction on the stream).
+__device__ __forceinline__ void clear_overflow(const SelArgs& a) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) *a.overflow = 0;
+}
 
 __device__ __forceinline__ bool is_cand(int j, int i, int sink) {
   return j < i && !(sink && j == 0);
@@ -189,6 +200,7 @@ __device__ float mass_ge(const float* s, const float* p, int nslots, int i, int 
 
 __global__ __launch_bounds__(256) void select_kernel(SelArgs a) {
   extern __shared__ float sm[];
+  clear_overflow(a);
   const int l = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row = blockIdx.x * (blockDim.x >> 6) + wave;
@@ -462,6 +474,7 @@ __device__ void topk_reg(const RowKeys<SPL>& r, int nsl, int nc, int k, unsigned
 // sigma gate's per-row part (its extra state stays out of the other forms).
 template <int SPL, bool FULL, bool SIG>
 __global__ __launch_bounds__(256) void select_reg_kernel(SelArgs a) {
+  clear_overflow(a);
   const bool use_b = FULL && a.use_b, use_p = FULL && a.use_p;
   const int l = lane_id();
   // (the wave index through readfirstlane: row, i and the slot count are then
@@ -784,15 +797,15 @@ __global__ __launch_bounds__(1024) void sigma_tile_kernel(const float* __restric
 
 // ------------------------------------------------------------------ CSR
 
-// row_ptr is clamped to the col_idx capacity, so a reader of the CSR can never
-// index past the buffer (the capacity bound makes the clamp a no-op).
 // Exclusive scan of the row counts in one workgroup: thread t owns a contiguous
 // chunk (a multiple of 4 rows, read and written as 16-byte vectors), the chunk
 // sums are scanned with wave shuffles and one LDS step across the 16 waves.
-// Offsets are clamped to the col_idx capacity.
+// Offsets are clamped to the col_idx capacity, so a reader of the CSR can never
+// index past the buffer; the capacity bound makes the clamp a no-op, and a total
+// past it (kept sets larger than the parameters allow) sets the overflow word.
 __global__ __launch_bounds__(1024) void scan_kernel(const int* __restrict__ counts,
                                                     int32_t* __restrict__ row_ptr, int rows,
-                                                    int64_t capacity) {
+                                                    int64_t capacity, int* __restrict__ overflow) {
   __shared__ int wsum[16];
   const int t = threadIdx.x, l = t & 63, w = t >> 6;
   const int chunk = (((rows + 1023) / 1024) + 3) & ~3;
@@ -836,7 +849,10 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int* __restrict__ coun
       }
     }
   }
-  if (t == 1023) row_ptr[rows] = clampc((int64_t)before + x);
+  if (t == 1023) {
+    row_ptr[rows] = clampc((int64_t)before + x);
+    *overflow = (int64_t)before + x > capacity ? 1 : 0;
+  }
 }
 
 // Sigma gate: a row whose tile fired also keeps its expansion blocks.
@@ -859,7 +875,8 @@ __global__ __launch_bounds__(256) void compact_kernel(const unsigned long long* 
                                                       uint8_t* __restrict__ gate_out,
                                                       const int32_t* __restrict__ row_ptr,
                                                       int32_t* __restrict__ col_idx, int rows,
-                                                      int nb, int nw, int64_t capacity, int width) {
+                                                      int nb, int nw, int64_t capacity, int width,
+                                                      int* __restrict__ overflow) {
   const int l = lane_id();
   const int row = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (row >= rows) return;
@@ -880,8 +897,10 @@ __global__ __launch_bounds__(256) void compact_kernel(const unsigned long long* 
     }
     run += __popcll(w);
   }
-  if (width > 0)
+  if (width > 0) {
     for (int p = run + l; p < width; p += 64) col_idx[base + p] = -1;
+    if (run > width && l == 0) *overflow = 1;
+  }
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -899,6 +918,8 @@ SelectWorkspace select_workspace_layout(const Shape& sh, bool export_scores, boo
   off += align256(rows * nw * sizeof(unsigned long long));
   w.counts_off = off;
   off += align256(rows * sizeof(int));
+  w.overflow_off = off;
+  off += 256;
   w.sigma_off = w.mask_x_off = w.counts_x_off = w.keys_off = w.fire_off = off;
   if (sigma_gate) {
     w.sigma_off = off;
@@ -915,6 +936,40 @@ SelectWorkspace select_workspace_layout(const Shape& sh, bool export_scores, boo
   w.total = off;
   return w;
 }
+
+namespace {
+
+// Slots per lane of the register form of the select kernel for rows of nb
+// blocks (0: rows too long, the LDS form runs).
+int select_slots(int nb, bool topk_only) {
+  const int nw = (nb + 63) / 64;
+  return nw <= 1 ? 1 : nw <= 2 ? 2 : nw <= 4 ? 4 : nw <= 8 ? 8 : nw <= 16 ? 16
+         : nw <= 32 ? 32 : nw <= 64 ? 64 : (nw <= 128 && topk_only) ? 128 : 0;
+}
+
+// The LDS form keeps each of its waves' rows in LDS: the scores, and the
+// rescue bounds and probabilities when those branches are on.
+size_t lds_row_bytes(int nb, bool use_b, bool use_p) {
+  return (size_t)((nb + 63) / 64) * 64 * sizeof(float) * (1 + (use_b ? 1 : 0) + (use_p ? 1 : 0));
+}
+
+int lds_form_waves(size_t row_bytes) {
+  const size_t w = 65536 / row_bytes;
+  return w < 1 ? 1 : (w > 4 ? 4 : (int)w);
+}
+
+constexpr size_t kLdsLimit = 160 * 1024;  // LDS of one CU on gfx950
+
+}  // namespace
+
+size_t select_lds_bytes(const Shape& sh, const SelectConfig& cfg) {
+  const bool use_b = cfg.rescue_fraction > 0.0, use_p = cfg.mass_threshold > 0.0f;
+  if (select_slots(sh.nb, !use_b && !use_p) > 0) return 0;
+  const size_t row = lds_row_bytes(sh.nb, use_b, use_p);
+  return (size_t)lds_form_waves(row) * row;
+}
+
+size_t select_lds_limit() { return kLdsLimit; }
 
 hipError_t launch_score_select(const Shape& sh, const SelectConfig& cfg, const float* q_centroid,
                                const float* q_norm, const float* k_centroid,
@@ -934,6 +989,22 @@ hipError_t launch_score_select(const Shape& sh, const SelectConfig& cfg, const f
   const int NT = (nb + 63) / 64;
 
   hipError_t e = hipSuccess;
+  // The LDS form beyond 64 KiB needs the kernel's dynamic LDS limit raised (once
+  // per device); done before the first launch so that a failure launches nothing.
+  const size_t lds_bytes = select_lds_bytes(sh, cfg);
+  if (lds_bytes > kLdsLimit) return hipErrorInvalidValue;  // rejected by the caller first
+  if (lds_bytes > 65536) {
+    static std::atomic<uint64_t> attr_set{0};
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    const uint64_t bit = 1ull << (dev & 63);
+    if (!(attr_set.load(std::memory_order_acquire) & bit)) {
+      e = hipFuncSetAttribute((const void*)select_kernel,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsLimit);
+      if (e != hipSuccess) return e;
+      attr_set.fetch_or(bit, std::memory_order_acq_rel);
+    }
+  }
   if (!scores_in) {
     hipLaunchKernelGGL(score_kernel, dim3(NT, NT, U), dim3(256), 0, stream, q_centroid,
                        k_centroid, scores, nb, sh.D, sh.G(), sh.per_group);
@@ -971,6 +1042,7 @@ hipError_t launch_score_select(const Shape& sh, const SelectConfig& cfg, const f
   a.sigma = sig ? (float*)(ws + w.sigma_off) : nullptr;
   a.mask_x = sig ? (unsigned long long*)(ws + w.mask_x_off) : nullptr;
   a.counts_x = sig ? (int*)(ws + w.counts_x_off) : nullptr;
+  a.overflow = (int*)(ws + w.overflow_off);
   // register form for rows up to 64*SPL = 4096 blocks (8192 with the top-k and
   // gate branches only), LDS form beyond.  When rows reach 64 slots the register
   // form runs once per range of query blocks [64*SPL/2, 64*SPL), each with the
@@ -978,8 +1050,7 @@ hipError_t launch_score_select(const Shape& sh, const SelectConfig& cfg, const f
   // longest rows first; with the top-k and gate branches only, the 32- to 128-slot
   // forms leave out the rescue and mass state.
   const bool topk_only = !a.use_b && !a.use_p;
-  const int spl = nw <= 1 ? 1 : nw <= 2 ? 2 : nw <= 4 ? 4 : nw <= 8 ? 8 : nw <= 16 ? 16
-                  : nw <= 32 ? 32 : nw <= 64 ? 64 : (nw <= 128 && topk_only) ? 128 : 0;
+  const int spl = select_slots(nb, topk_only);
 // one launch of the register form: N slots, FULL (every branch) or top-k only,
 // the sigma gate's form when it is on
 #define BSA_SELECT_REG(N, F)                                                          \
@@ -1019,10 +1090,9 @@ hipError_t launch_score_select(const Shape& sh, const SelectConfig& cfg, const f
     }
   } else {
     const size_t per_wave_bytes = (size_t)a.per_wave_floats * sizeof(float);
-    int waves = (int)(65536 / per_wave_bytes);
-    waves = waves < 1 ? 1 : (waves > 4 ? 4 : waves);
+    const int waves = lds_form_waves(per_wave_bytes);
     hipLaunchKernelGGL(select_kernel, dim3((rows + waves - 1) / waves), dim3(64 * waves),
-                       waves * per_wave_bytes, stream, a);
+                       lds_bytes, stream, a);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -1046,12 +1116,13 @@ hipError_t launch_score_select(const Shape& sh, const SelectConfig& cfg, const f
       if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, stream, counts, row_ptr, rows,
-                       col_capacity);
+                       col_capacity, a.overflow);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(compact_kernel, dim3((rows + 3) / 4), dim3(256), 0, stream, mask, a.mask_x,
-                     fire, gate_out, row_ptr, col_idx, rows, nb, nw, col_capacity, width);
+                     fire, gate_out, row_ptr, col_idx, rows, nb, nw, col_capacity, width,
+                     a.overflow);
   return hipGetLastError();
 }
 

@@ -70,7 +70,7 @@
 extern "C" {
 #endif
 
-#define BSA_ABI_VERSION 2
+#define BSA_ABI_VERSION 3
 
 typedef enum {
   BSA_OK = 0,
@@ -186,6 +186,11 @@ size_t bsa_score_select_workspace_size(const bsa_problem* problem,
  *   workspace    device scratch of at least
  *                bsa_score_select_workspace_size(problem, params, scores_out != NULL)
  *                bytes, else BSA_ERR_WORKSPACE.
+ * Rows longer than the select kernel's register form (4096 blocks; 8192 with
+ * the mass and rescue branches off) are kept in LDS, up to 160 KiB per row with
+ * the enabled branches (about 13600 blocks with mass and rescue, 20400 with one
+ * of them, 40900 with neither); longer rows return BSA_ERR_UNSUPPORTED.  The same
+ * limit applies to bsa_select_scores and bsa_score_select_padded.
  */
 bsa_status bsa_score_select(const bsa_problem* problem, const bsa_select_params* params,
                             const float* q_centroid, const float* q_norm,
@@ -193,6 +198,23 @@ bsa_status bsa_score_select(const bsa_problem* problem, const bsa_select_params*
                             int32_t* col_idx, int64_t col_capacity, float* scores_out,
                             float* bound_out, uint8_t* gate_out, void* workspace,
                             size_t workspace_bytes, void* hip_stream);
+
+/*
+ * Where the selection calls report a kept set that did not fit their output.
+ * Returns the byte offset, inside the workspace of bsa_score_select /
+ * bsa_select_scores / bsa_score_select_padded (sized with the same arguments;
+ * scores_given_or_exported as for the workspace size), of an int32 that each
+ * such call sets when its stream reaches the end of the call: 0 when every
+ * row's kept set was written in full, 1 when some row's kept blocks exceeded
+ * col_capacity (CSR: the row offsets are then clamped to col_capacity) or width
+ * (padded list: the row is cut at width).  With col_capacity and width at least
+ * the bounds the calls require this cannot happen for any input; the word
+ * exists so that a violation is visible instead of a silently shortened list.
+ * -1 on invalid arguments.  Reading it is the caller's business (after its own
+ * synchronisation); the library never reads it back.
+ */
+int64_t bsa_select_overflow_offset(const bsa_problem* problem, const bsa_select_params* params,
+                                   int scores_given_or_exported);
 
 /*
  * bsa_pool_key_bounds -- the Quest backbone's key-block summary ("Uncertainty-gated

@@ -78,6 +78,7 @@ def run_gpu(cfg, inp) -> GpuRun:
                                          1.0 / math.sqrt(cfg.head_dim), inp.q_scale, inp.k_scale,
                                          inp.v_scale)
         torch.cuda.synchronize()
+        assert not sel.overflowed(), "selection reported a kept set past the CSR capacity"
         rp = sel.row_ptr.cpu().numpy().astype(np.int64)
         ci = sel.col_idx[: int(rp[-1])].cpu().numpy().astype(np.int64)
         return GpuRun(out, lse, rp, ci, None, None, None, None, scores, None,
@@ -88,10 +89,41 @@ def run_gpu(cfg, inp) -> GpuRun:
                                      1.0 / math.sqrt(cfg.head_dim), inp.q_scale, inp.k_scale,
                                      inp.v_scale)
     torch.cuda.synchronize()
+    assert not sel.overflowed(), "selection reported a kept set past the CSR capacity"
     rp = sel.row_ptr.cpu().numpy().astype(np.int64)
     ci = sel.col_idx[: int(rp[-1])].cpu().numpy().astype(np.int64)
     return GpuRun(out, lse, rp, ci, pool.q_centroid, pool.q_norm, pool.k_centroid, pool.k_radius,
                   sel.scores, sel.bounds, sel.gate.cpu().numpy())
+
+
+def run_gpu_padded(cfg, inp, like: GpuRun) -> GpuRun:
+    """The padded-list path (selection written as kv_idx [U*nb, width], attention
+    reading it) on the same inputs, as a GpuRun whose CSR is the padded rows'
+    valid prefixes, so that check_all compares it with the oracle directly.
+    Pool outputs (or, for the Quest backbone, the scores and key bounds) come
+    from `like`, the CSR run of the same inputs."""
+    problem = bsa.make_problem(inp.q, inp.k, cfg.block_size, granularity_code(cfg))
+    params = lib_params(cfg)
+    if cfg.backbone == "quest":
+        pb = bsa.bsa_score_select_padded(problem, params, scores=like.scores, export=True)
+    else:
+        pool = bsa.PoolResult(like.qc, like.qn, like.kc, like.kr)
+        pb = bsa.bsa_score_select_padded(problem, params, pool=pool, export=True)
+    out, lse = bsa.bsa_attention_fwd_padded(problem, inp.q, inp.k, inp.v, pb.kv_idx,
+                                            1.0 / math.sqrt(cfg.head_dim), inp.q_scale,
+                                            inp.k_scale, inp.v_scale)
+    torch.cuda.synchronize()
+    assert not pb.overflowed(), "selection reported a kept set past the padded width"
+    kv = pb.kv_idx.cpu().numpy().astype(np.int64)
+    valid = kv >= 0
+    lens = valid.sum(axis=1)
+    # valid entries form a prefix of each row, then only sentinels
+    assert np.array_equal(valid, np.arange(kv.shape[1])[None, :] < lens[:, None])
+    rp = np.concatenate([[0], np.cumsum(lens)])
+    ci = kv[valid]
+    scores = like.scores if cfg.backbone == "quest" else pb.scores
+    return GpuRun(out, lse, rp, ci, like.qc, like.qn, like.kc, like.kr, scores, pb.bounds,
+                  pb.gate.cpu().numpy(), like.kmin, like.kmax)
 
 
 def _raw(t: torch.Tensor) -> np.ndarray:

@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.bsa_abi_version() == 2
+    assert lib.bsa_abi_version() == 3
     assert lib.bsa_status_string(0) == b"ok"
     assert lib.bsa_status_string(3) == b"CSR capacity too small"
 
@@ -106,6 +106,53 @@ def test_select_capacity_and_workspace_errors(lib):
     st = lib.bsa_score_select(ctypes.byref(p), ctypes.byref(s2), FAKE, None, FAKE, None, FAKE,
                               FAKE, cap2, None, None, None, FAKE, 10**12, None)
     assert st == 1
+
+
+@pytest.mark.parametrize("nb,kw", [
+    (14000, dict(mass_threshold=0.9, rescue_fraction=0.05)),  # 3 rows of floats per wave
+    (21000, dict(top_k=8, mass_threshold=0.9)),               # 2
+    (41000, dict(top_k=8)),                                   # 1
+])
+def test_select_rows_past_the_lds_limit_are_unsupported(lib, nb, kw):
+    """Rows too long for the register form are kept in LDS; beyond one CU's 160 KiB
+    the call is rejected on the host, before anything is launched."""
+    p = _prob(seq_len=nb * 128, num_q_heads=1, num_kv_heads=1)
+    s = bsa.make_params(**kw)
+    st = lib.bsa_score_select(ctypes.byref(p), ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE,
+                              FAKE, 10**12, None, None, None, FAKE, 10**12, None)
+    assert st == 2 and b"LDS" in lib.bsa_last_error()
+    st = lib.bsa_score_select_padded(ctypes.byref(p), ctypes.byref(s), FAKE, FAKE, FAKE, FAKE,
+                                     None, FAKE, nb, None, None, None, FAKE, 10**12, None)
+    assert st == 2
+    if "rescue_fraction" not in kw:
+        st = lib.bsa_select_scores(ctypes.byref(p), ctypes.byref(s), FAKE, FAKE, FAKE, 10**12,
+                                   None, FAKE, 10**12, None)
+        assert st == 2
+    # just inside the limit the same call gets past this check (and stops at the
+    # capacity check, before any launch)
+    p2 = _prob(seq_len=(nb * 97 // 100) * 128, num_q_heads=1, num_kv_heads=1)
+    cap = lib.bsa_csr_capacity_bound(ctypes.byref(p2), ctypes.byref(s))
+    st = lib.bsa_score_select(ctypes.byref(p2), ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE,
+                              FAKE, cap - 1, None, None, None, FAKE, 10**12, None)
+    assert st == 3
+
+
+def test_overflow_word_lies_inside_the_workspace(lib):
+    for kw, gate in ((dict(top_k=4, force_sink=1), 0), (dict(top_k=4, gate=2, gate_threshold=0.3), 2),
+                     (dict(mass_threshold=0.9, rescue_fraction=0.05), 0)):
+        p = _prob()
+        s = bsa.make_params(**kw)
+        for exported in (0, 1):
+            off = lib.bsa_select_overflow_offset(ctypes.byref(p), ctypes.byref(s), exported)
+            ws = lib.bsa_score_select_workspace_size(ctypes.byref(p), ctypes.byref(s), exported)
+            assert off >= 0 and off % 256 == 0 and off + 4 <= ws
+            wsp = lib.bsa_score_select_padded_workspace_size(ctypes.byref(p), ctypes.byref(s),
+                                                             exported)
+            assert off + 4 <= wsp
+        wss = lib.bsa_select_scores_workspace_size(ctypes.byref(p), ctypes.byref(s))
+        assert lib.bsa_select_overflow_offset(ctypes.byref(p), ctypes.byref(s), 1) + 4 <= wss
+    bad = bsa.make_params(top_k=-1)
+    assert lib.bsa_select_overflow_offset(ctypes.byref(_prob()), ctypes.byref(bad), 0) == -1
 
 
 def test_capacity_bound_covers_any_selection(lib):

@@ -104,3 +104,49 @@ def test_traffic_record_is_used_only_where_it_was_taken():
     assert bench.traffic_from_profile(h, w) == rec["hbm_bytes_per_launch"]
     assert bench.traffic_from_profile(h, "msa1m") is None
     assert bench.traffic_from_profile("0" * 16, w) is None
+
+
+def test_realized_stats_count_by_hand():
+    """Needle recall, planted-pair recall, gate rates and outlier recall on a
+    hand-built CSR (2 query heads over 1 kv head, 6 blocks)."""
+    cfg = _cfg(6 * 8, 8, 4, 2, 1)
+    cfg.force_sink = False
+    cfg.gate = "top12_gap"
+    nb = 6
+    rows = {  # (u, i) -> kept
+        (0, 0): [0], (0, 1): [0, 1], (0, 2): [1, 2], (0, 3): [0, 1, 3], (0, 4): [2, 4],
+        (0, 5): [1, 2, 3, 5], (1, 0): [0], (1, 1): [1], (1, 2): [1, 2], (1, 3): [3],
+        (1, 4): [1, 4], (1, 5): [5]}
+    counts = [len(rows[(u, i)]) for u in range(2) for i in range(nb)]
+    rp = np.concatenate([[0], np.cumsum(counts)])
+    ci = np.array([j for u in range(2) for i in range(nb) for j in rows[(u, i)]])
+    # needle block 1: eligible rows i > 1, both heads -> 8 pairs; kept in
+    # (0,2) (0,3) (0,5) (1,2) (1,4) -> 5
+    st = bench.realized_stats(cfg, {"needle_blocks": [1]}, rp, ci, None)
+    assert st["needle_pairs"] == 8 and st["needle_recall"] == round(5 / 8, 4)
+    # pairs (needle 1, decoy 2) planted in query blocks 3 and 5; gate fired on
+    # (0,3), (0,4), (1,5)
+    gate = np.zeros(2 * nb, dtype=np.uint8)
+    gate[[3, 4, nb + 5]] = 1
+    meta = {"pairs": {0: [(1, 2)]}, "planted_query_blocks": {0: {3: 0, 5: 0}}}
+    st = bench.realized_stats(cfg, meta, rp, ci, gate)
+    # planted rows: (0,3) needle yes decoy no; (0,5) both; (1,3) neither; (1,5) neither
+    assert st["planted_rows"] == 4
+    assert st["planted_needle_recall"] == 0.5 and st["planted_pair_recall"] == 0.25
+    assert st["gate_fire_rate_planted"] == 0.5  # (0,3) and (1,5)
+    assert st["gate_fire_rate_background"] == round(1 / 8, 4)  # (0,4)
+    # a wide block 2 whose outlier aims at query block 4 of head 0 (kept there),
+    # and block 3 aimed at block 5 of head 1 (not kept)
+    st = bench.realized_stats(cfg, {"wide_blocks": {0: {2: (17, 4, 0), 3: (30, 5, 1)}}},
+                              rp, ci, None)
+    assert st["outlier_rows"] == 2 and st["outlier_block_recall"] == 0.5
+
+
+def test_cpu_full_runs_the_whole_tiny_workload():
+    import torch
+    from workloads import config_by_name, generate, scaled
+    cfg = scaled(config_by_name("tiny"), 300)
+    inp = generate(cfg, "cpu")
+    res = bench.cpu_full(cfg, inp)
+    assert res["kind"] == "oracle" and res["value"] > 0 and res["cores"] >= 1
+    assert res["cpu_model"] and res["affinity_cores"] >= 1
