@@ -80,6 +80,7 @@ def load_library(path: str = LIB_PATH):
         "bsa_csr_capacity_bound": ([PP, PS], I64),
         "bsa_score_select_workspace_size": ([PP, PS, ctypes.c_int], SZ),
         "bsa_score_select": ([PP, PS, P, P, P, P, P, P, I64, P, P, P, P, SZ, P], ctypes.c_int),
+        "bsa_score_select_noalloc": ([PP, PS, P, P, P, P, P, P, I64, P, P, P, P], ctypes.c_int),
         "bsa_attention_fwd": ([PP, P, P, P, P, P, P, P, P, F, P, P, P], ctypes.c_int),
         "bsa_pool_key_bounds": ([PP, P, P, P, P, P], ctypes.c_int),
         "bsa_quest_scores_workspace_size": ([PP], SZ),
@@ -248,6 +249,21 @@ def bsa_score_select(problem: Problem, params: SelectParams, pool: PoolResult, e
                               _ptr(b.bounds), _ptr(b.gate), _ptr(b.workspace),
                               b.workspace.numel(), _stream(dev)))
     return Selection(b.row_ptr, b.col_idx, None, b.scores, b.bounds, b.gate, b)
+
+
+def bsa_score_select_noalloc(problem: Problem, params: SelectParams, pool: PoolResult,
+                             export=False, buffers: SelectBuffers | None = None) -> Selection:
+    """bsa_score_select on the library's own fixed scratch instead of a workspace
+    (for callers that cannot allocate; the buffers' workspace is not used)."""
+    L = load_library()
+    dev = pool.q_centroid.device
+    b = buffers or SelectBuffers(problem, params, dev, export)
+    _check(L.bsa_score_select_noalloc(ctypes.byref(problem), ctypes.byref(params),
+                                      _ptr(pool.q_centroid), _ptr(pool.q_norm),
+                                      _ptr(pool.k_centroid), _ptr(pool.k_radius), _ptr(b.row_ptr),
+                                      _ptr(b.col_idx), b.capacity, _ptr(b.scores), _ptr(b.bounds),
+                                      _ptr(b.gate), _stream(dev)))
+    return Selection(b.row_ptr, b.col_idx, None, b.scores, b.bounds, b.gate, None)
 
 
 def bsa_pool_key_bounds(problem: Problem, k, k_scale=None, out=None):

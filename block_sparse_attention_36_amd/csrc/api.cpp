@@ -237,24 +237,28 @@ size_t bsa_score_select_workspace_size(const bsa_problem* problem, const bsa_sel
       .total;
 }
 
-bsa_status bsa_score_select(const bsa_problem* problem, const bsa_select_params* params,
-                            const float* q_centroid, const float* q_norm,
-                            const float* k_centroid, const float* k_radius, int32_t* row_ptr,
-                            int32_t* col_idx, int64_t col_capacity, float* scores_out,
-                            float* bound_out, uint8_t* gate_out, void* workspace,
-                            size_t workspace_bytes, void* hip_stream) {
-  bsa::Shape sh;
+namespace {
+
+// Everything bsa_score_select checks except the workspace; fills sh and the
+// workspace bytes the call needs.
+bsa_status check_score_select(const bsa_problem* problem, const bsa_select_params* params,
+                              const float* q_centroid, const float* q_norm,
+                              const float* k_centroid, const float* k_radius,
+                              const int32_t* row_ptr, const int32_t* col_idx,
+                              int64_t col_capacity, const float* scores_out, bsa::Shape& sh,
+                              size_t& need) {
   bsa_status st = check_problem(problem, sh);
   if (st != BSA_OK) return st;
   st = check_params(params);
   if (st != BSA_OK) return st;
   st = check_select_form(sh, params);
   if (st != BSA_OK) return st;
-  if (sh.S == 0) return ok();
+  need = 0;
+  if (sh.S == 0) return BSA_OK;
   if (!q_centroid || !k_centroid || !row_ptr || !col_idx)
     return fail(BSA_ERR_INVALID_ARGUMENT, "q_centroid, k_centroid, row_ptr and col_idx are required");
-  if (((uintptr_t)q_centroid | (uintptr_t)k_centroid | (uintptr_t)row_ptr | (uintptr_t)workspace) & 15)
-    return fail(BSA_ERR_INVALID_ARGUMENT, "q_centroid, k_centroid, row_ptr and workspace must be 16-byte aligned");
+  if (((uintptr_t)q_centroid | (uintptr_t)k_centroid | (uintptr_t)row_ptr) & 15)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "q_centroid, k_centroid and row_ptr must be 16-byte aligned");
   const bool rescue = params->rescue_fraction > 0.0;
   if (rescue && (!q_norm || !k_radius))
     return fail(BSA_ERR_INVALID_ARGUMENT, "the rescue branch needs q_norm and k_radius");
@@ -264,18 +268,74 @@ bsa_status bsa_score_select(const bsa_problem* problem, const bsa_select_params*
   if (col_capacity < bound)
     return fail(BSA_ERR_CAPACITY, "col_capacity %lld < bound %lld", (long long)col_capacity,
                 (long long)bound);
-  const size_t need =
-      bsa::select_workspace_layout(sh, scores_out != nullptr, params->gate == BSA_GATE_SIGMA_CUT)
-          .total;
-  if (!workspace || workspace_bytes < need)
-    return fail(BSA_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, need);
+  need = bsa::select_workspace_layout(sh, scores_out != nullptr, params->gate == BSA_GATE_SIGMA_CUT)
+             .total;
+  return BSA_OK;
+}
+
+bsa_status launch_checked_score_select(const bsa::Shape& sh, const bsa_select_params* params,
+                                       const float* q_centroid, const float* q_norm,
+                                       const float* k_centroid, const float* k_radius,
+                                       int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                                       float* scores_out, float* bound_out, uint8_t* gate_out,
+                                       void* workspace, void* hip_stream, const char* what) {
+  const bool rescue = params->rescue_fraction > 0.0;
   const bsa::SelectConfig cfg = select_config(params);
   return device_status(
       bsa::launch_score_select(sh, cfg, q_centroid, rescue ? q_norm : nullptr, k_centroid,
                                rescue ? k_radius : nullptr, row_ptr, col_idx, col_capacity,
                                scores_out, rescue ? bound_out : nullptr, gate_out, workspace,
                                (hipStream_t)hip_stream),
-      "bsa_score_select launch");
+      what);
+}
+
+}  // namespace
+
+bsa_status bsa_score_select(const bsa_problem* problem, const bsa_select_params* params,
+                            const float* q_centroid, const float* q_norm,
+                            const float* k_centroid, const float* k_radius, int32_t* row_ptr,
+                            int32_t* col_idx, int64_t col_capacity, float* scores_out,
+                            float* bound_out, uint8_t* gate_out, void* workspace,
+                            size_t workspace_bytes, void* hip_stream) {
+  bsa::Shape sh;
+  size_t need = 0;
+  bsa_status st = check_score_select(problem, params, q_centroid, q_norm, k_centroid, k_radius,
+                                     row_ptr, col_idx, col_capacity, scores_out, sh, need);
+  if (st != BSA_OK) return st;
+  if (sh.S == 0) return ok();
+  if ((uintptr_t)workspace & 15)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+  if (!workspace || workspace_bytes < need)
+    return fail(BSA_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, need);
+  return launch_checked_score_select(sh, params, q_centroid, q_norm, k_centroid, k_radius,
+                                     row_ptr, col_idx, col_capacity, scores_out, bound_out,
+                                     gate_out, workspace, hip_stream, "bsa_score_select launch");
+}
+
+bsa_status bsa_score_select_noalloc(const bsa_problem* problem, const bsa_select_params* params,
+                                    const float* q_centroid, const float* q_norm,
+                                    const float* k_centroid, const float* k_radius,
+                                    int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                                    float* scores_out, float* bound_out, uint8_t* gate_out,
+                                    void* hip_stream) {
+  bsa::Shape sh;
+  size_t need = 0;
+  bsa_status st = check_score_select(problem, params, q_centroid, q_norm, k_centroid, k_radius,
+                                     row_ptr, col_idx, col_capacity, scores_out, sh, need);
+  if (st != BSA_OK) return st;
+  if (sh.S == 0) return ok();
+  if (need > bsa::select_scratch_bytes())
+    return fail(BSA_ERR_WORKSPACE,
+                "this selection needs %zu bytes of scratch; the allocation-free entry point "
+                "holds %zu (with scores_out given the score matrix stays out of it)",
+                need, bsa::select_scratch_bytes());
+  void* scratch = nullptr;
+  const hipError_t e = bsa::select_scratch(&scratch);
+  if (e != hipSuccess) return device_status(e, "bsa_score_select_noalloc scratch lookup");
+  return launch_checked_score_select(sh, params, q_centroid, q_norm, k_centroid, k_radius,
+                                     row_ptr, col_idx, col_capacity, scores_out, bound_out,
+                                     gate_out, scratch, hip_stream,
+                                     "bsa_score_select_noalloc launch");
 }
 
 bsa_status bsa_pool_key_bounds(const bsa_problem* problem, const void* k, const float* k_scale,

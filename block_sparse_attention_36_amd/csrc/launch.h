@@ -40,6 +40,11 @@ SelectWorkspace select_workspace_layout(const Shape& sh, bool export_scores, boo
 size_t select_lds_bytes(const Shape& sh, const SelectConfig& cfg);
 size_t select_lds_limit();
 
+// The allocation-free selection's scratch: its size, and its address on the
+// current device (looked up on the first call per device).
+size_t select_scratch_bytes();
+hipError_t select_scratch(void** ptr);
+
 // scores_in != nullptr: selection on the given scores [U, nb, nb] (no centroid
 // scores are computed; q_centroid and k_centroid are unused).  width > 0: the
 // output is the padded list col_idx[rows][width] (row_ptr unused), else CSR.

@@ -31,6 +31,7 @@
 // CSR: a single-workgroup exclusive scan of the row counts, then one wave per row
 // writes the set bits of its mask in ascending order.
 #include <atomic>
+#include <mutex>
 
 #include "common.h"
 #include "launch.h"
@@ -970,6 +971,42 @@ size_t select_lds_bytes(const Shape& sh, const SelectConfig& cfg) {
 }
 
 size_t select_lds_limit() { return kLdsLimit; }
+
+// ---- scratch of the allocation-free selection entry point
+//
+// One fixed array per GPU, in place of a caller's workspace, for callers that
+// cannot allocate device memory.  Each GPU the library runs on holds it until
+// the process ends; every call on a GPU shares that GPU's copy (calls that
+// overlap on one GPU race).  Nothing in it has to start zeroed: every word a
+// selection reads back was written earlier in the same call.
+namespace {
+constexpr size_t kScratchBytes = size_t(64) << 20;
+constexpr int kMaxDevices = 64;
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+size_t select_scratch_bytes() { return kScratchBytes; }
+
+hipError_t select_scratch(void** ptr) {
+  // device address of `scratch` on the current device, looked up once per device
+  // (the array's name in host code is a host-side stand-in, not that address)
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_score_select(const Shape& sh, const SelectConfig& cfg, const float* q_centroid,
                                const float* q_norm, const float* k_centroid,

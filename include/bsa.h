@@ -200,6 +200,33 @@ bsa_status bsa_score_select(const bsa_problem* problem, const bsa_select_params*
                             size_t workspace_bytes, void* hip_stream);
 
 /*
+ * bsa_score_select_noalloc -- bsa_score_select without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  It computes exactly what
+ * bsa_score_select computes, with the same kernels and the same arguments
+ * otherwise, but keeps its scratch (the score matrix when scores_out is NULL,
+ * the kept-block masks and counts, the sigma gate's tile buffers, the overflow
+ * word) in one fixed array of 64 MiB that the library holds on each GPU it runs
+ * on until the process ends.  It calls no allocating routine.
+ *
+ *   Limit: a selection needing more than 64 MiB of scratch (that is
+ *   bsa_score_select_workspace_size(problem, params, scores_out != NULL)) returns
+ *   BSA_ERR_WORKSPACE before anything is launched; passing scores_out moves the
+ *   U*nb*nb score matrix out of the scratch.
+ *   Sharing: every call on one GPU uses that GPU's single array, which keeps the
+ *   last call's contents; calls that overlap on one GPU (two streams, two host
+ *   threads) race and must be serialised by the caller.  Nothing in the array
+ *   needs to start zeroed.  The overflow word of this call lives in the array and
+ *   is not exposed.
+ */
+bsa_status bsa_score_select_noalloc(const bsa_problem* problem, const bsa_select_params* params,
+                                    const float* q_centroid, const float* q_norm,
+                                    const float* k_centroid, const float* k_radius,
+                                    int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                                    float* scores_out, float* bound_out, uint8_t* gate_out,
+                                    void* hip_stream);
+
+/*
  * Where the selection calls report a kept set that did not fit their output.
  * Returns the byte offset, inside the workspace of bsa_score_select /
  * bsa_select_scores / bsa_score_select_padded (sized with the same arguments;
