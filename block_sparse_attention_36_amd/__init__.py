@@ -23,7 +23,8 @@ import os
 from dataclasses import dataclass
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libbsa.so")
+# BSA_LIBRARY overrides the in-tree build (e.g. the sanitized build of the C ABI)
+LIB_PATH = os.environ.get("BSA_LIBRARY") or os.path.join(_HERE, "libbsa.so")
 
 BSA_OK = 0
 BSA_BF16, BSA_FP8_E4M3 = 0, 1

@@ -69,6 +69,36 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
     return LIB
 
 
+def build_sanitized(verbose: bool = False) -> str:
+    """libbsa_sanitized.so: the C ABI layer (api.cpp) compiled for the host alone by
+    g++ with AddressSanitizer and UndefinedBehaviorSanitizer, linked with the
+    regular kernel objects (built first if missing).  Only the host validation and
+    sizing code is instrumented; load it with the ASan runtime preloaded
+    (LD_PRELOAD) and point the binding at it with BSA_LIBRARY."""
+    os.makedirs(BUILD, exist_ok=True)
+    kernels = [s for s in SOURCES if s.endswith(".hip")]
+    objs = [os.path.join(BUILD, s + ".o") for s in kernels]
+    if not all(os.path.exists(o) for o in objs):
+        build(verbose=verbose)
+    rocm = os.path.dirname(os.path.dirname(hipcc()))
+    api_obj = os.path.join(BUILD, "api_sanitized.o")
+    san = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+           "-fno-omit-frame-pointer"]
+    cmd = ["g++", "-O1", "-g", "-std=c++17", "-fPIC", *san, "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(rocm, "include"), "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+           "-c", os.path.join(CSRC, "api.cpp"), "-o", api_obj]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"sanitized api.cpp failed:\n{' '.join(cmd)}\n{res.stderr}")
+    out = os.path.join(BUILD, "libbsa_sanitized.so")
+    cmd = ["g++", "-shared", *san, api_obj, *objs, "-L", os.path.join(rocm, "lib"), "-lamdhip64",
+           "-Wl,-rpath," + os.path.join(rocm, "lib"), "-o", out]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"linking the sanitized library failed:\n{' '.join(cmd)}\n{res.stderr}")
+    return out
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=None)
