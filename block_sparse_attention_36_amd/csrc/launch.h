@@ -29,6 +29,7 @@ struct SelectConfig {
 // Workspace carve-up used by launch_score_select (byte offsets, 256-aligned).
 struct SelectWorkspace {
   size_t scores_off, mask_off, counts_off, overflow_off;
+  size_t run_sum_off, run_off_off;  // per-64-row count sums and their scanned offsets
   size_t sigma_off, mask_x_off, counts_x_off, keys_off, fire_off;  // sigma gate only
   size_t total;
 };

@@ -797,13 +797,29 @@ __global__ __launch_bounds__(1024) void sigma_tile_kernel(const float* __restric
 }
 
 // ------------------------------------------------------------------ CSR
+//
+// Row offsets in three steps: the kept counts are summed per run of 64 rows (one
+// wave per run), one workgroup scans the run sums, and the compaction, one wave
+// per row, adds the counts of the rows before it in its run (one coalesced load
+// and a wave sum) to its run's offset.
 
-// Exclusive scan of the row counts in one workgroup: thread t owns a contiguous
-// chunk (a multiple of 4 rows, read and written as 16-byte vectors), the chunk
-// sums are scanned with wave shuffles and one LDS step across the 16 waves.
-// Offsets are clamped to the col_idx capacity, so a reader of the CSR can never
-// index past the buffer; the capacity bound makes the clamp a no-op, and a total
-// past it (kept sets larger than the parameters allow) sets the overflow word.
+__global__ __launch_bounds__(256) void run_sum_kernel(const int* __restrict__ counts,
+                                                      int* __restrict__ run_sum, int rows) {
+  const int l = lane_id();
+  const int run = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (run * 64 >= rows) return;
+  const int r = run * 64 + l;
+  const int c = wave_sum_int(r < rows ? counts[r] : 0);
+  if (l == 0) run_sum[run] = c;
+}
+
+// Exclusive scan of the run sums (`rows` values here) in one workgroup: thread t
+// owns a contiguous chunk (a multiple of 4 values, read and written as 16-byte
+// vectors), the chunk sums are scanned with wave shuffles and one LDS step across
+// the 16 waves; the total goes to row_ptr[rows].  Offsets are clamped to the
+// col_idx capacity, so a reader of the CSR can never index past the buffer; the
+// capacity bound makes the clamp a no-op, and a total past it (kept sets larger
+// than the parameters allow) sets the overflow word.
 __global__ __launch_bounds__(1024) void scan_kernel(const int* __restrict__ counts,
                                                     int32_t* __restrict__ row_ptr, int rows,
                                                     int64_t capacity, int* __restrict__ overflow) {
@@ -865,16 +881,22 @@ __global__ __launch_bounds__(256) void expand_counts_kernel(int* __restrict__ co
   if (row < rows && fire[row % nb]) counts[row] += counts_x[row];
 }
 
-// One wave per row writes the set bits of its mask in ascending order.  With the
-// sigma gate, rows of fired tiles add their expansion bits (disjoint from the
-// kept bits) and the row's gate flag is its tile's decision.  With width > 0 the
-// output is the padded list instead of CSR: row r occupies [r*width, (r+1)*width),
-// its blocks ascending and then -1 sentinels, with no scan.
+// One wave per row writes the set bits of its mask in ascending order: the row's
+// mask words are loaded 64 at a time, one per lane, and the non-zero ones visited
+// in order, each set bit's lane writing its block.  With the sigma gate, rows of
+// fired tiles add their expansion bits (disjoint from the kept bits) and the
+// row's gate flag is its tile's decision.  CSR: the row's offset is its run's
+// scanned offset plus the counts of the rows before it in the run (clamped to the
+// capacity like the run offsets), written to row_ptr here.  With width > 0 the
+// output is the padded list instead: row r occupies [r*width, (r+1)*width), its
+// blocks ascending and then -1 sentinels, with no scan.
 __global__ __launch_bounds__(256) void compact_kernel(const unsigned long long* __restrict__ mask,
                                                       const unsigned long long* __restrict__ mask_x,
                                                       const uint8_t* __restrict__ fire,
                                                       uint8_t* __restrict__ gate_out,
-                                                      const int32_t* __restrict__ row_ptr,
+                                                      const int* __restrict__ counts,
+                                                      const int32_t* __restrict__ run_off,
+                                                      int32_t* __restrict__ row_ptr,
                                                       int32_t* __restrict__ col_idx, int rows,
                                                       int nb, int nw, int64_t capacity, int width,
                                                       int* __restrict__ overflow) {
@@ -883,20 +905,41 @@ __global__ __launch_bounds__(256) void compact_kernel(const unsigned long long* 
   if (row >= rows) return;
   const int i = row % nb;
   const int nslots = i / 64 + 1;
-  const int64_t base = width > 0 ? (int64_t)row * width : row_ptr[row];
-  if (width > 0) capacity = base + width;
+  int64_t base;
+  if (width > 0) {
+    base = (int64_t)row * width;
+    capacity = base + width;
+  } else {
+    const int r0 = row & ~63, k = row - r0;
+    const int before = wave_sum_int(l < k ? counts[r0 + l] : 0);
+    base = (int64_t)run_off[row >> 6] + before;
+    if (l == 0) {
+      row_ptr[row] = (int32_t)(base < capacity ? base : capacity);
+      if (row == rows - 1) row_ptr[rows] = run_off[(rows + 63) >> 6];
+    }
+  }
   const bool expand = fire != nullptr && fire[i];
   if (fire != nullptr && gate_out != nullptr && l == 0) gate_out[row] = expand ? 1 : 0;
   int run = 0;
   const unsigned long long lt = lanemask_lt();
-  for (int e = 0; e < nslots; ++e) {
-    const unsigned long long w =
-        mask[(size_t)row * nw + e] | (expand ? mask_x[(size_t)row * nw + e] : 0ull);
-    if ((w >> l) & 1ull) {
-      const int64_t pos = base + run + __popcll(w & lt);
-      if (pos < capacity) col_idx[pos] = e * 64 + l;
+  const unsigned long long* mrow = mask + (size_t)row * nw;
+  const unsigned long long* xrow = expand ? mask_x + (size_t)row * nw : nullptr;
+  for (int e0 = 0; e0 < nslots; e0 += 64) {
+    const int e = e0 + l;
+    const unsigned long long mine = e < nslots ? (mrow[e] | (xrow ? xrow[e] : 0ull)) : 0ull;
+    unsigned long long nz = __ballot(mine != 0ull);
+    while (nz) {
+      const int f = __builtin_ctzll(nz);
+      nz &= nz - 1;
+      const unsigned lo = __builtin_amdgcn_readlane((unsigned)mine, f);
+      const unsigned hi = __builtin_amdgcn_readlane((unsigned)(mine >> 32), f);
+      const unsigned long long w = ((unsigned long long)hi << 32) | lo;
+      if ((w >> l) & 1ull) {
+        const int64_t pos = base + run + __popcll(w & lt);
+        if (pos < capacity) col_idx[pos] = (e0 + f) * 64 + l;
+      }
+      run += __popcll(w);
     }
-    run += __popcll(w);
   }
   if (width > 0) {
     for (int p = run + l; p < width; p += 64) col_idx[base + p] = -1;
@@ -921,6 +964,11 @@ SelectWorkspace select_workspace_layout(const Shape& sh, bool export_scores, boo
   off += align256(rows * sizeof(int));
   w.overflow_off = off;
   off += 256;
+  const size_t nrun = (rows + 63) / 64;
+  w.run_sum_off = off;
+  off += align256(nrun * sizeof(int));
+  w.run_off_off = off;
+  off += align256((nrun + 1) * sizeof(int));
   w.sigma_off = w.mask_x_off = w.counts_x_off = w.keys_off = w.fire_off = off;
   if (sigma_gate) {
     w.sigma_off = off;
@@ -1145,6 +1193,8 @@ hipError_t launch_score_select(const Shape& sh, const SelectConfig& cfg, const f
     if (e != hipSuccess) return e;
   }  // (with the top-k branch off the select kernel writes gate_out = 0 itself)
 
+  int* run_sum = (int*)(ws + w.run_sum_off);
+  int32_t* run_off = (int32_t*)(ws + w.run_off_off);
   if (width == 0) {
     if (fire) {
       hipLaunchKernelGGL(expand_counts_kernel, dim3((rows + 255) / 256), dim3(256), 0, stream,
@@ -1152,14 +1202,19 @@ hipError_t launch_score_select(const Shape& sh, const SelectConfig& cfg, const f
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, stream, counts, row_ptr, rows,
+    const int nrun = (rows + 63) / 64;
+    hipLaunchKernelGGL(run_sum_kernel, dim3((nrun + 3) / 4), dim3(256), 0, stream, counts,
+                       run_sum, rows);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, stream, run_sum, run_off, nrun,
                        col_capacity, a.overflow);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(compact_kernel, dim3((rows + 3) / 4), dim3(256), 0, stream, mask, a.mask_x,
-                     fire, gate_out, row_ptr, col_idx, rows, nb, nw, col_capacity, width,
-                     a.overflow);
+                     fire, gate_out, counts, run_off, row_ptr, col_idx, rows, nb, nw,
+                     col_capacity, width, a.overflow);
   return hipGetLastError();
 }
 
