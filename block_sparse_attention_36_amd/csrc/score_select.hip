@@ -42,57 +42,87 @@ namespace {
 
 // ------------------------------------------------------------------ scores
 
-// One workgroup of four waves per 64 x 64 tile of the causal lower triangle
-// (wave w: the 32 x 32 sub-tile (w / 2, w % 2)).  The tile's 64 query and 64 key
-// centroids are staged through LDS 32 dimensions at a time with coalesced
-// 16-byte loads; rows are padded to 33 floats so the per-lane operand reads of
-// one MFMA (32 rows, one column) hit distinct banks.
+// One workgroup of four waves per 128 x 128 tile of the causal lower triangle;
+// wave w computes the 64 x 64 sub-tile (w / 2, w % 2) as 2 x 2 products of 32 x 32,
+// so every operand read from LDS feeds two products.  The tile's 128 query and
+// 128 key centroids are staged through LDS 32 dimensions at a time with
+// coalesced 16-byte loads; rows are padded to 33 floats so the per-lane operand
+// reads of one product (32 rows, one column) hit distinct banks.  Each score is
+// accumulated over the dimensions in ascending pairs, one V_MFMA_F32_32X32X2_F32
+// step per pair.  The grid enumerates the lower-triangle tiles only (tile t of
+// row it = the largest with it(it+1)/2 <= t), so consecutive workgroups, which
+// the dispatcher deals round-robin to the eight XCDs, spread the work evenly; a
+// square grid with the upper tiles exiting would give XCD k only the tile rows
+// it = k (mod 8).
 __global__ __launch_bounds__(256) void score_kernel(const float* __restrict__ qc,
                                                     const float* __restrict__ kc,
                                                     float* __restrict__ scores, int nb, int D,
                                                     int G, int per_group) {
-  const int it = blockIdx.x, jt = blockIdx.y, u = blockIdx.z;
-  if (jt > it) return;  // uniform for the workgroup
-  __shared__ float As[64 * 33], Bs[64 * 33];
+  const int t = blockIdx.x, u = blockIdx.y;
+  int it = (int)((sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
+  while ((it + 1) * (it + 2) / 2 <= t) ++it;  // float rounding, either way
+  while (it * (it + 1) / 2 > t) --it;
+  const int jt = t - it * (it + 1) / 2;
+  __shared__ float As[128 * 33], Bs[128 * 33];
   const int tid = threadIdx.x, l = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wi = w >> 1, wj = w & 1, hf = l >> 5;
   const int g = per_group ? u : u / G;
-  f32x16 acc = {0};
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y) acc[x][y] = f32x16{0};
+  // the next 32 dimensions are loaded into registers while the current ones
+  // are multiplied
+  f32x4 av[4], bv[4];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4) {
+      const int idx = tid + 256 * t4, row = idx >> 3, c4 = (idx & 7) * 4;
+      const int ia = min(it * 128 + row, nb - 1), jb = min(jt * 128 + row, nb - 1);
+      av[t4] = *(const f32x4*)(qc + ((size_t)u * nb + ia) * D + k0 + c4);
+      bv[t4] = *(const f32x4*)(kc + ((size_t)g * nb + jb) * D + k0 + c4);
+    }
+  };
+  load(0);
   for (int k0 = 0; k0 < D; k0 += 32) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int idx = tid + 256 * t, row = idx >> 3, c4 = (idx & 7) * 4;
-      const int ia = min(it * 64 + row, nb - 1), jb = min(jt * 64 + row, nb - 1);
-      const f32x4 av = *(const f32x4*)(qc + ((size_t)u * nb + ia) * D + k0 + c4);
-      const f32x4 bv = *(const f32x4*)(kc + ((size_t)g * nb + jb) * D + k0 + c4);
+    for (int t4 = 0; t4 < 4; ++t4) {
+      const int idx = tid + 256 * t4, row = idx >> 3, c4 = (idx & 7) * 4;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        As[row * 33 + c4 + e] = av[e];
-        Bs[row * 33 + c4 + e] = bv[e];
+        As[row * 33 + c4 + e] = av[t4][e];
+        Bs[row * 33 + c4 + e] = bv[t4][e];
       }
     }
     __syncthreads();
-    // A: row wi*32 + l%32, B: column wj*32 + l%32; lane half hf takes k = 2s + hf
-    const float* ar = As + (wi * 32 + (l & 31)) * 33 + hf;
-    const float* br = Bs + (wj * 32 + (l & 31)) * 33 + hf;
-    float av[16], bv[16];  // all operands of the chunk requested before the first product
+    if (k0 + 32 < D) load(k0 + 32);
+    // A: rows wi*64 + 32x + l%32, B: columns wj*64 + 32y + l%32; lane half hf
+    // takes k = 2s + hf of step s
+    const float* ar = As + (wi * 64 + (l & 31)) * 33 + hf;
+    const float* br = Bs + (wj * 64 + (l & 31)) * 33 + hf;
 #pragma unroll
     for (int st = 0; st < 16; ++st) {
-      av[st] = ar[2 * st];
-      bv[st] = br[2 * st];
+      const float a0 = ar[2 * st], a1 = ar[32 * 33 + 2 * st];
+      const float b0 = br[2 * st], b1 = br[32 * 33 + 2 * st];
+      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0][0], 0, 0, 0);
+      acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc[0][1], 0, 0, 0);
+      acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
+      acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
     }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int st = 0; st < 16; ++st)
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[st], bv[st], acc, 0, 0, 0);
     __syncthreads();
   }
-  const int j = jt * 64 + wj * 32 + (l & 31);
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int i = it * 64 + wi * 32 + (v >> 2) * 8 + hf * 4 + (v & 3);
-    if (i < nb && j <= i) scores[((size_t)u * nb + i) * nb + j] = acc[v];
-  }
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y) {
+      const int j = jt * 128 + wj * 64 + y * 32 + (l & 31);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int i = it * 128 + wi * 64 + x * 32 + (v >> 2) * 8 + hf * 4 + (v & 3);
+        if (i < nb && j <= i) scores[((size_t)u * nb + i) * nb + j] = acc[x][y][v];
+      }
+    }
 }
 
 // ------------------------------------------------------------------ selection
@@ -1071,7 +1101,7 @@ hipError_t launch_score_select(const Shape& sh, const SelectConfig& cfg, const f
   unsigned long long* mask = (unsigned long long*)(ws + w.mask_off);
   int* counts = (int*)(ws + w.counts_off);
   const int nb = sh.nb, U = sh.U(), rows = U * nb, nw = (nb + 63) / 64;
-  const int NT = (nb + 63) / 64;
+  const int NT = (nb + 127) / 128;  // score tiles per side
 
   hipError_t e = hipSuccess;
   // The LDS form beyond 64 KiB needs the kernel's dynamic LDS limit raised (once
@@ -1091,7 +1121,7 @@ hipError_t launch_score_select(const Shape& sh, const SelectConfig& cfg, const f
     }
   }
   if (!scores_in) {
-    hipLaunchKernelGGL(score_kernel, dim3(NT, NT, U), dim3(256), 0, stream, q_centroid,
+    hipLaunchKernelGGL(score_kernel, dim3(NT * (NT + 1) / 2, U), dim3(256), 0, stream, q_centroid,
                        k_centroid, scores, nb, sh.D, sh.G(), sh.per_group);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
