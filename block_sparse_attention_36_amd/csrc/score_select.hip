@@ -35,6 +35,7 @@
 
 #include "common.h"
 #include "launch.h"
+#include "slot_bits.h"
 
 namespace bsa {
 
@@ -429,19 +430,6 @@ __global__ __launch_bounds__(256) void select_kernel(SelArgs a) {
 // cross-lane reduction; the base branch extracts maxima one at a time in the
 // ranking order (the usual case needs a handful) and falls back to bisection
 // on fixed-tree mass sums when more than 16 blocks are needed.
-
-// One bit per register slot of a lane, in as many 64-bit words as SPL needs.
-template <int SPL>
-struct SlotBits {
-  static constexpr int NWD = (SPL + 63) / 64;
-  unsigned long long w[NWD];
-  __device__ __forceinline__ void clear() {
-#pragma unroll
-    for (int q = 0; q < NWD; ++q) w[q] = 0ull;
-  }
-  __device__ __forceinline__ bool get(int e) const { return (w[e >> 6] >> (e & 63)) & 1ull; }
-  __device__ __forceinline__ void set(int e) { w[e >> 6] |= 1ull << (e & 63); }
-};
 
 template <int SPL>
 struct RowKeys {
