@@ -476,9 +476,32 @@ __device__ void topk_reg(const RowKeys<SPL>& r, int nsl, int nc, int k, unsigned
     need = 0;
     return;
   }
-  // (early exit as in topk_threshold: exactly k candidates >= x decide the set)
+  // Bisection for the largest key t with at least k candidates >= t (early exit
+  // as in topk_threshold: exactly k candidates >= x decide the set).  For k <= 64
+  // it starts below the bits that the k-th largest lane maximum m and the largest
+  // key share: t lies in [m, max] (k lanes hold a key >= m), so the full bisection
+  // would set exactly those bits (probes at or below m count >= k, above max count
+  // 0) and only then reach the bits where m and max differ.  The lane maxima are
+  // ranked by ballots, which cost a compare and a popcount per probe instead of a
+  // pass over every slot.
   unsigned t = 0u;
-  for (int bit = 31; bit >= 0; --bit) {
+  int top = 31;
+  if (k <= 64) {
+    unsigned lm = 0u;  // non-candidate slots hold key 0
+#pragma unroll
+    for (int e = 0; e < SPL; ++e)
+      if (e < nsl) lm = max(lm, r.k[e]);
+    unsigned m = 0u;
+    for (int bit = 31; bit >= 0; --bit) {
+      const unsigned x = m | (1u << bit);
+      if (__popcll(ballot64(lm >= x)) >= k) m = x;
+    }
+    const unsigned kmax = wave_max_uint(lm);
+    const unsigned diff = m ^ kmax;
+    top = diff ? 31 - __builtin_clz(diff) : -1;
+    t = top < 0 ? m : (top == 31 ? 0u : (m & ~((2u << top) - 1u)));
+  }
+  for (int bit = top; bit >= 0; --bit) {
     const unsigned x = t | (1u << bit);
     const int c = count_ge_reg(r, nsl, x);
     if (c >= k) t = x;
