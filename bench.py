@@ -398,7 +398,7 @@ ATTN_KERNEL = "attn_whole_kernel"
 
 # How the counter record is made (run from /tmp with TMPDIR=/tmp; $R is the repository).
 PMC_COMMANDS = [
-    "rocprofv3 --pmc {c} --kernel-include-regex \"attn_|pool_|select_|score_|copy|scan_|compact_\" "
+    "rocprofv3 --pmc {c} --kernel-include-regex \"attn_|pool_|select_|score_|copy|scan_|compact_|run_sum_\" "
     "--output-format csv -d $R/gpurun_out/pmc_{d} -o run -- python3 $R/bench.py --steps 1 --warmup 1 "
     "--no-cpu-baseline --calibrate-copy".format(c=c, d=d)
     for c, d in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write"))
@@ -410,7 +410,7 @@ def summarize_pmc(fetch_dir: str, write_dir: str, out_json: str) -> int:
     """HBM bytes per attention launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
     each scaled by what the same counter reads for a plain copy of COPY_BYTES."""
     import statistics
-    out = {"kernel": "attn_whole_kernel<128, 128, false>", "workload": "dual128k",
+    out = {"kernel": "attn_whole_kernel<128, 128, false, false>", "workload": "dual128k",
            "kernel_source_hash": source_hash("attention.hip", "common.h"),
            "commands": PMC_COMMANDS}
     others = {}
@@ -431,8 +431,8 @@ def summarize_pmc(fetch_dir: str, write_dir: str, out_json: str) -> int:
         for r in rows:
             name = r["Kernel_Name"]
             short = next((k for k in ("pool_q_kernel", "pool_k_kernel", "score_kernel",
-                                      "select_reg_kernel", "select_kernel", "scan_kernel",
-                                      "compact_kernel") if k in name), None)
+                                      "select_reg_kernel", "select_kernel", "run_sum_kernel",
+                                      "scan_kernel", "compact_kernel") if k in name), None)
             if short:
                 others.setdefault(short, {}).setdefault(counter.lower(), []).append(
                     float(r["Counter_Value"]) * 1024 / factor)
@@ -548,6 +548,10 @@ def main(argv=None) -> int:
         pbufs = bsa.PaddedBuffers(problem, params, dev, export=False, given_scores=quest)
     else:
         bufs = bsa.SelectBuffers(problem, params, dev, export=False, given_scores=quest)
+    # E4M3 V is expanded to its exact bf16 values inside each step (a lossless change
+    # of format), and attention reads those; the padded-list path reads the codes
+    expand = cfg.dtype == "fp8" and not padded
+    v16 = torch.empty(inp.v.shape, dtype=torch.bfloat16, device=dev) if expand else None
     out = torch.empty(cfg.seq_len, cfg.num_q_heads, cfg.head_dim, dtype=torch.bfloat16, device=dev)
     lse = torch.empty(cfg.num_q_heads, cfg.seq_len, dtype=torch.float32, device=dev)
     scale = 1.0 / math.sqrt(cfg.head_dim)
@@ -578,9 +582,17 @@ def main(argv=None) -> int:
             sel = bsa.bsa_score_select(problem, params, pool, buffers=bufs)
         if ev:
             ev[2].record()
+        if expand:
+            bsa.bsa_expand_e4m3(problem, inp.v, out=v16)
+        if ev:
+            ev[5].record()
         if padded:
             bsa.bsa_attention_fwd_padded(problem, inp.q, inp.k, inp.v, pbufs.kv_idx, scale,
                                          inp.q_scale, inp.k_scale, inp.v_scale, out=out, lse=lse)
+        elif expand:
+            bsa.bsa_attention_fwd_expanded_v(problem, inp.q, inp.k, v16, sel.row_ptr, sel.col_idx,
+                                             scale, inp.q_scale, inp.k_scale, inp.v_scale,
+                                             out=out, lse=lse)
         else:
             bsa.bsa_attention_fwd(problem, inp.q, inp.k, inp.v, sel.row_ptr, sel.col_idx, scale,
                                   inp.q_scale, inp.k_scale, inp.v_scale, out=out, lse=lse)
@@ -592,7 +604,7 @@ def main(argv=None) -> int:
         step()
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -612,7 +624,8 @@ def main(argv=None) -> int:
     kept_flops = attention_flops(rp, ci, cfg)
     pool_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     sel_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
-    att_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
+    exp_ms = np.array([e[2].elapsed_time(e[5]) for e in evs])
+    att_ms = np.array([e[5].elapsed_time(e[3]) for e in evs])
     ms_per_step = wall * 1e3 / args.steps
     attn_avg = float(att_ms.mean())
     achieved = kept_flops / (attn_avg * 1e-3) / 1e12
@@ -651,10 +664,12 @@ def main(argv=None) -> int:
                      "peak_basis": peak_basis,
                      "frac_of_bf16_peak": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_from_profile(khash, cfg.name),
-                     "kernel": f"{ATTN_KERNEL}<{cfg.head_dim},{cfg.block_size},{str(cfg.dtype == 'fp8').lower()}>",
+                     "kernel": f"{ATTN_KERNEL}<{cfg.head_dim},{cfg.block_size},"
+                               f"{str(cfg.dtype == 'fp8').lower()},{str(expand).lower()}>",
                      "kernel_source_hash": khash},
         "stages_ms": {"pool": round(float(pool_ms.mean()), 4),
                       "score_select": round(float(sel_ms.mean()), 4),
+                      **({"expand_v": round(float(exp_ms.mean()), 4)} if expand else {}),
                       "attention": round(attn_avg, 4)},
         "frac_of_bf16_peak_whole_step": round(kept_flops / (ms_per_step * 1e-3) / 1e12
                                               / PEAK_BF16_TFLOPS, 4),

@@ -83,6 +83,8 @@ def load_library(path: str = LIB_PATH):
         "bsa_score_select": ([PP, PS, P, P, P, P, P, P, I64, P, P, P, P, SZ, P], ctypes.c_int),
         "bsa_score_select_noalloc": ([PP, PS, P, P, P, P, P, P, I64, P, P, P, P], ctypes.c_int),
         "bsa_attention_fwd": ([PP, P, P, P, P, P, P, P, P, F, P, P, P], ctypes.c_int),
+        "bsa_expand_e4m3": ([PP, P, P, P], ctypes.c_int),
+        "bsa_attention_fwd_expanded_v": ([PP, P, P, P, P, P, P, P, P, F, P, P, P], ctypes.c_int),
         "bsa_pool_key_bounds": ([PP, P, P, P, P, P], ctypes.c_int),
         "bsa_quest_scores_workspace_size": ([PP], SZ),
         "bsa_quest_scores": ([PP, P, P, P, P, P, P, SZ, P], ctypes.c_int),
@@ -410,6 +412,36 @@ def bsa_attention_fwd(problem: Problem, q, k, v, row_ptr, col_idx, softmax_scale
     return out, (lse if want_lse else None)
 
 
+def bsa_expand_e4m3(problem: Problem, v, out=None):
+    """The E4M3 V codes [S, Hkv, D] as their exact bf16 values (v_scale not applied)."""
+    import torch
+    L = load_library()
+    if out is None:
+        out = torch.empty(v.shape, dtype=torch.bfloat16, device=v.device)
+    _check(L.bsa_expand_e4m3(ctypes.byref(problem), _ptr(_u8(v)), _ptr(out), _stream(v.device)))
+    return out
+
+
+def bsa_attention_fwd_expanded_v(problem: Problem, q, k, v_bf16, row_ptr, col_idx,
+                                 softmax_scale=None, q_scale=None, k_scale=None, v_scale=None,
+                                 want_lse=True, out=None, lse=None):
+    """bsa_attention_fwd for E4M3 inputs with V given as bsa_expand_e4m3's bf16 values."""
+    import torch
+    L = load_library()
+    S, Hq, D = q.shape
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty(S, Hq, D, dtype=torch.bfloat16, device=q.device)
+    if want_lse and lse is None:
+        lse = torch.empty(Hq, S, dtype=torch.float32, device=q.device)
+    _check(L.bsa_attention_fwd_expanded_v(
+        ctypes.byref(problem), _ptr(_u8(q)), _ptr(_u8(k)), _ptr(v_bf16), _ptr(q_scale),
+        _ptr(k_scale), _ptr(v_scale), _ptr(row_ptr), _ptr(col_idx), float(softmax_scale),
+        _ptr(out), _ptr(lse) if want_lse else None, _stream(q.device)))
+    return out, (lse if want_lse else None)
+
+
 def prefill_quest(q, k, v, block_size: int, params: SelectParams, granularity=BSA_SEL_PER_QHEAD,
                   q_scale=None, k_scale=None, v_scale=None, softmax_scale=None, export=False):
     """One layer on the Quest backbone: key bounds -> tile scores -> select -> attention.
@@ -430,6 +462,11 @@ def prefill(q, k, v, block_size: int, params: SelectParams, granularity=BSA_SEL_
     rescue = params.rescue_fraction > 0
     pool = bsa_pool(problem, q, k, q_scale, k_scale, want_norm=rescue, want_radius=rescue)
     sel = bsa_score_select(problem, params, pool, export=export)
-    out, lse = bsa_attention_fwd(problem, q, k, v, sel.row_ptr, sel.col_idx, softmax_scale,
-                                 q_scale, k_scale, v_scale)
+    if problem.dtype == BSA_FP8_E4M3:  # V codes expanded to bf16 once, attention reads those
+        out, lse = bsa_attention_fwd_expanded_v(problem, q, k, bsa_expand_e4m3(problem, v),
+                                                sel.row_ptr, sel.col_idx, softmax_scale,
+                                                q_scale, k_scale, v_scale)
+    else:
+        out, lse = bsa_attention_fwd(problem, q, k, v, sel.row_ptr, sel.col_idx, softmax_scale,
+                                     q_scale, k_scale, v_scale)
     return out, lse, sel, pool

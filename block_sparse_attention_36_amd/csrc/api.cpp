@@ -545,4 +545,45 @@ bsa_status bsa_attention_fwd(const bsa_problem* problem, const void* q, const vo
                        "bsa_attention_fwd launch");
 }
 
+bsa_status bsa_expand_e4m3(const bsa_problem* problem, const void* v, void* v_bf16,
+                           void* hip_stream) {
+  bsa::Shape sh;
+  bsa_status st = check_problem(problem, sh);
+  if (st != BSA_OK) return st;
+  if (!sh.fp8) return fail(BSA_ERR_INVALID_ARGUMENT, "only E4M3 problems have codes to expand");
+  if (sh.S == 0) return ok();
+  if (!v || !v_bf16) return fail(BSA_ERR_INVALID_ARGUMENT, "v and v_bf16 are required");
+  if (misaligned(v) || misaligned(v_bf16))
+    return fail(BSA_ERR_INVALID_ARGUMENT, "v and v_bf16 must be 16-byte aligned");
+  return device_status(bsa::launch_expand_e4m3(sh, v, v_bf16, (hipStream_t)hip_stream),
+                       "bsa_expand_e4m3 launch");
+}
+
+bsa_status bsa_attention_fwd_expanded_v(const bsa_problem* problem, const void* q, const void* k,
+                                        const void* v_bf16, const float* q_scale,
+                                        const float* k_scale, const float* v_scale,
+                                        const int32_t* row_ptr, const int32_t* col_idx,
+                                        float softmax_scale, void* out, float* lse,
+                                        void* hip_stream) {
+  bsa::Shape sh;
+  bsa_status st = check_problem(problem, sh);
+  if (st != BSA_OK) return st;
+  if (!sh.fp8)
+    return fail(BSA_ERR_INVALID_ARGUMENT,
+                "bsa_attention_fwd_expanded_v is for E4M3 problems; use bsa_attention_fwd");
+  if (sh.S == 0) return ok();
+  if (!q || !k || !v_bf16 || !row_ptr || !col_idx || !out)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "q, k, v_bf16, row_ptr, col_idx and out are required");
+  if (!q_scale || !k_scale || !v_scale)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "FP8 inputs need q_scale, k_scale and v_scale");
+  if (!std::isfinite(softmax_scale) || softmax_scale <= 0.f)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and > 0");
+  if (misaligned(q) || misaligned(k) || misaligned(v_bf16) || misaligned(out))
+    return fail(BSA_ERR_INVALID_ARGUMENT, "q, k, v_bf16 and out must be 16-byte aligned");
+  return device_status(bsa::launch_attention(sh, q, k, v_bf16, q_scale, k_scale, v_scale, row_ptr,
+                                             col_idx, softmax_scale, out, lse,
+                                             (hipStream_t)hip_stream, 0, true),
+                       "bsa_attention_fwd_expanded_v launch");
+}
+
 }  // extern "C"

@@ -38,7 +38,10 @@
 // codes are exact in fp32, so this is the bf16 result at twice the rate), with K
 // read raw from LDS and Q held raw in registers; V is expanded to bf16 in LDS
 // (exact) for O^T = V^T P^T.  q_scale and k_scale fold into the per-block logit
-// scale and v_scale into the probabilities.
+// scale and v_scale into the probabilities.  When the caller has expanded the V
+// codes to bf16 beforehand (exactly, with the library's expansion kernel), the
+// V tiles are copied straight into LDS as bf16 and the per-block expansion and
+// its barrier drop out; the results are the same bit for bit.
 #include <atomic>
 
 #include "common.h"
@@ -266,10 +269,12 @@ struct WTiles {
   }
 };
 
-template <int D, int B, bool FP8>
+template <int D, int B, bool FP8, bool V16>
 __global__ __launch_bounds__(64 * (B / 32), 2) void attn_whole_kernel(AttnArgs a) {
   typedef WCfg<D, B> C;
   typedef WTiles<D, B, FP8> ST;
+  typedef WTiles<D, B, false> SV;  // V tiles given as bf16 (E4M3 codes expanded beforehand)
+  static_assert(!V16 || FP8, "bf16 V is the E4M3 path's option");
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   const int tid = threadIdx.x, l = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -321,11 +326,20 @@ __global__ __launch_bounds__(64 * (B / 32), 2) void attn_whole_kernel(AttnArgs a
   auto blk = [](int j) { return j < 0 ? 0 : j; };
   unsigned doff[ST::NI];
   ST::plan(a, wave, l, doff);
+  unsigned voff[V16 ? SV::NI : 1];
+  if (V16) SV::plan(a, wave, l, voff);
+  // V(j): raw tile (then expanded in LDS), or the bf16 tile straight into place
+  auto issue_v = [&](int j) {
+    if (V16)
+      SV::issue(a, a.v, g, j, lds + ST::XV, wave, voff);
+    else
+      ST::issue(a, a.v, g, j, lds + ST::VBUF, wave, doff);
+  };
   if (nblk > 0) {
     load_chunk(0);
     const int j0 = blk(id_at(0));
     ST::issue(a, a.k, g, j0, lds + ST::KBUF, wave, doff);
-    ST::issue(a, a.v, g, j0, lds + ST::VBUF, wave, doff);
+    issue_v(j0);
   }
 
   // ---- Q fragments (B operand of S^T = K Q^T), query column = lane % 32.
@@ -485,11 +499,11 @@ __global__ __launch_bounds__(64 * (B / 32), 2) void attn_whole_kernel(AttnArgs a
     lds_barrier();
     if (n + 1 < nblk) ST::issue(a, a.k, g, jn, lds + ST::KBUF, wave, doff);
     const unsigned char* vt = lds + ST::VBUF;
-    if (FP8) {
+    if (FP8 && !V16) {
       ST::expand_v(lds + ST::VBUF, lds + ST::XV, tid);
       lds_barrier();
-      vt = lds + ST::XV;
     }
+    if (FP8) vt = lds + ST::XV;
 #pragma unroll
     for (int kt2 = 0; kt2 < C::NKT; ++kt2) pv_tile<D, B>(vt + vrow0, pk[kt2], o, kt2, rlo, cb0);
 
@@ -497,7 +511,7 @@ __global__ __launch_bounds__(64 * (B / 32), 2) void attn_whole_kernel(AttnArgs a
     __builtin_amdgcn_s_setprio(0);
     wait_vmem_all();
     lds_barrier();
-    if (n + 1 < nblk) ST::issue(a, a.v, g, jn, lds + ST::VBUF, wave, doff);
+    if (n + 1 < nblk) issue_v(jn);
   }
 
   // ---- output: this wave owns its 32 queries outright
@@ -519,7 +533,7 @@ __global__ __launch_bounds__(64 * (B / 32), 2) void attn_whole_kernel(AttnArgs a
   }
 }
 
-template <int D, int B, bool FP8>
+template <int D, int B, bool FP8, bool V16 = false>
 hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
   typedef WTiles<D, B, FP8> WT;
   static_assert(WT::LDS_BYTES <= 80 * 1024, "two workgroups per CU must fit the 160 KiB LDS");
@@ -531,23 +545,44 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
   (void)hipGetDevice(&dev);
   const uint64_t bit = 1ull << (dev & 63);
   if (!(attr_set.load(std::memory_order_acquire) & bit)) {
-    const hipError_t e = hipFuncSetAttribute((const void*)attn_whole_kernel<D, B, FP8>,
+    const hipError_t e = hipFuncSetAttribute((const void*)attn_whole_kernel<D, B, FP8, V16>,
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
                                              WT::LDS_BYTES);
     if (e != hipSuccess) return e;
     attr_set.fetch_or(bit, std::memory_order_acq_rel);
   }
-  hipLaunchKernelGGL((attn_whole_kernel<D, B, FP8>), dim3(rows8 * 8 * G), dim3(WCfg<D, B>::NT),
+  hipLaunchKernelGGL((attn_whole_kernel<D, B, FP8, V16>), dim3(rows8 * 8 * G), dim3(WCfg<D, B>::NT),
                      WT::LDS_BYTES, stream, a);
   return hipGetLastError();
 }
 
+// E4M3 codes -> bf16, exactly (every E4M3 value is a bf16 value): 16 codes per
+// thread, one 16-byte load and two 16-byte stores.
+__global__ __launch_bounds__(256) void expand_e4m3_kernel(const u32x4* __restrict__ codes,
+                                                          u32x4* __restrict__ out, int64_t n16) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= n16) return;
+  const u32x4 w = codes[t];
+  const u32x2 a = e4m3x4_to_bf16x4(w[0]), b = e4m3x4_to_bf16x4(w[1]);
+  const u32x2 c = e4m3x4_to_bf16x4(w[2]), d = e4m3x4_to_bf16x4(w[3]);
+  out[2 * t] = u32x4{a[0], a[1], b[0], b[1]};
+  out[2 * t + 1] = u32x4{c[0], c[1], d[0], d[1]};
+}
+
 }  // namespace
+
+hipError_t launch_expand_e4m3(const Shape& sh, const void* codes, void* out, hipStream_t stream) {
+  const int64_t n16 = sh.S * sh.Hkv * sh.D / 16;  // D is a multiple of 16
+  if (n16 == 0) return hipSuccess;
+  hipLaunchKernelGGL(expand_e4m3_kernel, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, stream,
+                     (const u32x4*)codes, (u32x4*)out, n16);
+  return hipGetLastError();
+}
 
 hipError_t launch_attention(const Shape& sh, const void* q, const void* k, const void* v,
                             const float* q_scale, const float* k_scale, const float* v_scale,
                             const int32_t* row_ptr, const int32_t* col_idx, float softmax_scale,
-                            void* out, float* lse, hipStream_t stream, int width) {
+                            void* out, float* lse, hipStream_t stream, int width, bool v16) {
   AttnArgs a;
   a.q = q;
   a.k = k;
@@ -566,9 +601,11 @@ hipError_t launch_attention(const Shape& sh, const void* q, const void* k, const
   a.per_group = sh.per_group;
   a.width = width;
   a.scale_log2 = softmax_scale * kLog2e;
-#define BSA_ATTN(DD, BB) \
-  if (sh.D == DD && sh.B == BB) \
-    return sh.fp8 ? launch_t<DD, BB, true>(a, stream) : launch_t<DD, BB, false>(a, stream);
+#define BSA_ATTN(DD, BB)                                                               \
+  if (sh.D == DD && sh.B == BB)                                                       \
+    return !sh.fp8 ? launch_t<DD, BB, false>(a, stream)                                \
+                   : v16 ? launch_t<DD, BB, true, true>(a, stream)                     \
+                         : launch_t<DD, BB, true>(a, stream);
   BSA_ATTN(128, 128)
   BSA_ATTN(128, 64)
   BSA_ATTN(64, 64)

@@ -69,6 +69,10 @@ hipError_t launch_quest_scores(const Shape& sh, const void* q, const float* q_sc
 hipError_t launch_attention(const Shape& sh, const void* q, const void* k, const void* v,
                             const float* q_scale, const float* k_scale, const float* v_scale,
                             const int32_t* row_ptr, const int32_t* col_idx, float softmax_scale,
-                            void* out, float* lse, hipStream_t stream, int width = 0);
+                            void* out, float* lse, hipStream_t stream, int width = 0,
+                            bool v16 = false);
+
+// E4M3 V codes [S, Hkv, D] -> their exact bf16 values in the same layout.
+hipError_t launch_expand_e4m3(const Shape& sh, const void* codes, void* out, hipStream_t stream);
 
 }  // namespace bsa

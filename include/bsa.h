@@ -70,7 +70,7 @@
 extern "C" {
 #endif
 
-#define BSA_ABI_VERSION 3
+#define BSA_ABI_VERSION 4
 
 typedef enum {
   BSA_OK = 0,
@@ -367,6 +367,35 @@ bsa_status bsa_attention_fwd(const bsa_problem* problem, const void* q, const vo
                              const float* v_scale, const int32_t* row_ptr,
                              const int32_t* col_idx, float softmax_scale, void* out,
                              float* lse, void* hip_stream);
+
+/*
+ * bsa_expand_e4m3 -- the V codes of an E4M3 problem as bf16 values, for
+ * bsa_attention_fwd_expanded_v.  Every E4M3 value is exactly a bf16 value, so
+ * this is a lossless change of format; v_scale is not applied (it stays a
+ * separate argument of the attention call).
+ *
+ *   v        E4M3 codes [S, Hkv, D] (16-byte aligned).
+ *   v_bf16   out bf16 [S, Hkv, D] (16-byte aligned, 2*S*Hkv*D bytes, owned by the
+ *            caller).
+ * BSA_ERR_INVALID_ARGUMENT for a BF16 problem (no codes) or missing pointers.
+ */
+bsa_status bsa_expand_e4m3(const bsa_problem* problem, const void* v, void* v_bf16,
+                           void* hip_stream);
+
+/*
+ * bsa_attention_fwd_expanded_v -- bsa_attention_fwd for an E4M3 problem whose V
+ * is given as its exact bf16 expansion (bsa_expand_e4m3); q, k and every scale
+ * as for bsa_attention_fwd, the results equal its results bit for bit (same
+ * passages).  The V tiles then go straight into LDS in the form the P V products
+ * read, instead of being expanded there block by block.
+ * BSA_ERR_INVALID_ARGUMENT for a BF16 problem (call bsa_attention_fwd).
+ */
+bsa_status bsa_attention_fwd_expanded_v(const bsa_problem* problem, const void* q, const void* k,
+                                        const void* v_bf16, const float* q_scale,
+                                        const float* k_scale, const float* v_scale,
+                                        const int32_t* row_ptr, const int32_t* col_idx,
+                                        float softmax_scale, void* out, float* lse,
+                                        void* hip_stream);
 
 #ifdef __cplusplus
 }

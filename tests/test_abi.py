@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.bsa_abi_version() == 3
+    assert lib.bsa_abi_version() == 4
     assert lib.bsa_status_string(0) == b"ok"
     assert lib.bsa_status_string(3) == b"CSR capacity too small"
 
@@ -312,3 +312,30 @@ def test_binding_raises_without_library(tmp_path):
             bsa.load_library(str(tmp_path / "missing.so"))
     finally:
         bsa._lib = saved
+
+
+def test_expanded_v_entry_points_reject_bf16_problems_and_missing_pointers(lib):
+    """The E4M3 V expansion and the attention on expanded V are E4M3-only; every
+    check fails before a device call (the fake pointers are never touched)."""
+    p = _prob()  # BF16
+    assert lib.bsa_expand_e4m3(ctypes.byref(p), FAKE, FAKE, None) == 1
+    assert b"E4M3" in lib.bsa_last_error()
+    st = lib.bsa_attention_fwd_expanded_v(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                          FAKE, FAKE, 0.1, FAKE, None, None)
+    assert st == 1 and b"bsa_attention_fwd" in lib.bsa_last_error()
+    q8 = _prob(dtype=bsa.BSA_FP8_E4M3)
+    assert lib.bsa_expand_e4m3(ctypes.byref(q8), None, FAKE, None) == 1
+    assert lib.bsa_expand_e4m3(ctypes.byref(q8), ctypes.c_void_p(0x1004), FAKE, None) == 1
+    assert b"aligned" in lib.bsa_last_error()
+    # scales are required, the softmax scale must be positive
+    st = lib.bsa_attention_fwd_expanded_v(ctypes.byref(q8), FAKE, FAKE, FAKE, None, FAKE, FAKE,
+                                          FAKE, FAKE, 0.1, FAKE, None, None)
+    assert st == 1
+    st = lib.bsa_attention_fwd_expanded_v(ctypes.byref(q8), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                          FAKE, FAKE, -1.0, FAKE, None, None)
+    assert st == 1
+    # an empty sequence is a no-op before any pointer is looked at
+    e8 = _prob(dtype=bsa.BSA_FP8_E4M3, seq_len=0)
+    assert lib.bsa_expand_e4m3(ctypes.byref(e8), None, None, None) == 0
+    assert lib.bsa_attention_fwd_expanded_v(ctypes.byref(e8), None, None, None, None, None, None,
+                                            None, None, 0.1, None, None, None) == 0

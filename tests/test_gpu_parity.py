@@ -282,3 +282,40 @@ def test_repeat_runs_are_bitwise_identical():
     b = K.run_gpu(cfg, inp)
     assert np.array_equal(a.row_ptr, b.row_ptr) and np.array_equal(a.col_idx, b.col_idx)
     assert torch.equal(a.out, b.out) and torch.equal(a.lse, b.lse)
+
+
+# E4M3 shapes (every (head_dim, block_size) pair, ragged tails, both granularities)
+# and the 1M workload at full size for the expanded-V attention
+EXPANDED_V = [c for c in SHAPES if c.dtype == "fp8"] + [
+    scaled(config_by_name("dual128k_fp8"), 4096 + 77, num_q_heads=8, num_kv_heads=2),
+    config_by_name("msa1m")]
+
+
+@pytest.mark.parametrize("cfg", EXPANDED_V, ids=[c.name for c in EXPANDED_V])
+def test_expanded_v_attention_equals_the_codes_path(cfg):
+    """bsa_expand_e4m3 decodes every code exactly (against torch's E4M3 decoding),
+    and attention on the expanded V equals attention on the codes bit for bit
+    (outputs and log-sum-exp), so the oracle parity of the codes path carries over."""
+    _gpu_or_skip()
+    import block_sparse_attention_36_amd as bsa
+    import bsa_check as K
+    print(f"[expanded-v] {cfg.name} S={cfg.seq_len} Hq={cfg.num_q_heads} Hkv={cfg.num_kv_heads}",
+          flush=True)
+    inp = generate(cfg, "cpu" if cfg.seq_len < 100000 else "cuda").to("cuda")
+    problem = bsa.make_problem(inp.q, inp.k, cfg.block_size, K.granularity_code(cfg))
+    params = K.lib_params(cfg)
+    pool = bsa.bsa_pool(problem, inp.q, inp.k, inp.q_scale, inp.k_scale)
+    sel = bsa.bsa_score_select(problem, params, pool)
+    v16 = bsa.bsa_expand_e4m3(problem, inp.v)
+    ref16 = inp.v.view(torch.float8_e4m3fn).float().to(torch.bfloat16)
+    assert torch.equal(v16.view(torch.int16), ref16.view(torch.int16))
+    del ref16
+    scale = 1.0 / math.sqrt(cfg.head_dim)
+    out0, lse0 = bsa.bsa_attention_fwd(problem, inp.q, inp.k, inp.v, sel.row_ptr, sel.col_idx,
+                                       scale, inp.q_scale, inp.k_scale, inp.v_scale)
+    out1, lse1 = bsa.bsa_attention_fwd_expanded_v(problem, inp.q, inp.k, v16, sel.row_ptr,
+                                                  sel.col_idx, scale, inp.q_scale, inp.k_scale,
+                                                  inp.v_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out0.view(torch.int16), out1.view(torch.int16))
+    assert torch.equal(lse0, lse1)
