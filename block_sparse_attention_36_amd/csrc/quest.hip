@@ -84,7 +84,6 @@ struct QCfg {
   static constexpr int BUF = CH * LROW;       // bytes per LDS buffer
   static constexpr int PIECES = CH * ROW / 16;
   static constexpr int PPT = PIECES / NT;     // 16-byte pieces per thread per chunk
-  static constexpr int LDS_BYTES = 2 * BUF + 2 * NW * 32 * 4;
   static_assert(PIECES % NT == 0, "chunk pieces must divide among the threads");
 };
 
@@ -94,26 +93,27 @@ __device__ __forceinline__ unsigned neg_mask(unsigned x) {
   return ((x >> 15) & 0x00010001u) * 0xFFFFu;
 }
 
-template <int D, int B, bool FP8, int NP>
+// HP heads of one kv head per workgroup pass: every bounds fragment read from LDS
+// feeds HP products, and the chunk staging and barrier serve HP heads.
+template <int D, int B, bool FP8, int NP, int HP>
 __global__ __launch_bounds__(64 * (B / 32), 2) void quest_score_kernel(QuestArgs a) {
   typedef QCfg<D, B, NP> C;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-  float* red = (float*)(lds + 2 * C::BUF);  // [2][NW][32]
+  float* red = (float*)(lds + 2 * C::BUF);  // [2][NW][HP][32]
   const int tid = threadIdx.x, l = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = a.Hq / a.Hkv, nb = a.nb;
-  const int Gu = a.per_group ? 1 : G;  // selection units per kv head
+  const int Gu = a.per_group ? 1 : G / HP;  // workgroups per (kv head, query block)
   const int bid = blockIdx.x;
   const int xcd = bid & 7, t8 = bid >> 3;
   const int hh = t8 % Gu;
   const int r = (t8 / Gu) * 8 + xcd;
   if (r >= a.Hkv * nb) return;  // padding workgroup (uniform: no barrier reached)
   const int g = r / nb, i = nb - 1 - r % nb;
-  const int u = a.per_group ? g : g * G + hh;
-  const int nheads = a.per_group ? G : 1;
+  const int nheads = a.per_group ? G : HP;  // heads this workgroup covers, HP per pass
+  const int hbase = a.per_group ? g * G : g * G + hh * HP;
   const int nch = i / C::CH + 1;
   const unsigned char* kp = (const unsigned char*)(a.packed + (size_t)g * nb * NP * D);
-  float* srow = a.scores + ((size_t)u * nb + i) * nb;
 
   u32x4 pf[C::PPT];
   auto stage_load = [&](int c) {
@@ -135,35 +135,39 @@ __global__ __launch_bounds__(64 * (B / 32), 2) void quest_score_kernel(QuestArgs
     }
   };
 
-  for (int hx = 0; hx < nheads; ++hx) {
-    const int h = a.per_group ? g * G + hx : u;
-    if (hx > 0) __syncthreads();  // the previous head's last reduction has read red[]
+  for (int hx = 0; hx < nheads; hx += HP) {
+    if (hx > 0) __syncthreads();  // the previous pass's last reduction has read red[]
     // A fragments: row (l & 31) of this wave's 32, coordinates 16s + 8(l >> 5) + [0, 8)
     const int64_t t = (int64_t)i * B + wave * 32 + (l & 31);
     const bool rv = t < a.S;
-    u32x4 qp[C::NS], qn[C::NS];
+    u32x4 qp[HP][C::NS], qn[HP][C::NS];
+    float qs[HP];
 #pragma unroll
-    for (int s = 0; s < C::NS; ++s) {
-      const int d0 = 16 * s + 8 * (l >> 5);
-      u32x4 x = u32x4{0u, 0u, 0u, 0u};
-      if (rv) {
-        const size_t e0 = ((size_t)t * a.Hq + h) * D + d0;
-        if (FP8) {
-          const u32x2 c8 = *(const u32x2*)((const unsigned char*)a.q + e0);
-          const u32x2 lo = e4m3x4_to_bf16x4(c8[0]), hi = e4m3x4_to_bf16x4(c8[1]);
-          x = u32x4{lo[0], lo[1], hi[0], hi[1]};
-        } else {
-          x = *(const u32x4*)((const unsigned char*)a.q + e0 * 2);
+    for (int hp = 0; hp < HP; ++hp) {
+      const int h = hbase + hx + hp;
+      qs[hp] = FP8 ? a.q_scale[(size_t)h * nb + i] : 1.0f;
+#pragma unroll
+      for (int s = 0; s < C::NS; ++s) {
+        const int d0 = 16 * s + 8 * (l >> 5);
+        u32x4 x = u32x4{0u, 0u, 0u, 0u};
+        if (rv) {
+          const size_t e0 = ((size_t)t * a.Hq + h) * D + d0;
+          if (FP8) {
+            const u32x2 c8 = *(const u32x2*)((const unsigned char*)a.q + e0);
+            const u32x2 lo = e4m3x4_to_bf16x4(c8[0]), hi = e4m3x4_to_bf16x4(c8[1]);
+            x = u32x4{lo[0], lo[1], hi[0], hi[1]};
+          } else {
+            x = *(const u32x4*)((const unsigned char*)a.q + e0 * 2);
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const unsigned m = neg_mask(x[e]);
+          qn[hp][s][e] = x[e] & m;
+          qp[hp][s][e] = x[e] & ~m;
         }
       }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const unsigned m = neg_mask(x[e]);
-        qn[s][e] = x[e] & m;
-        qp[s][e] = x[e] & ~m;
-      }
     }
-    const float qs = FP8 ? a.q_scale[(size_t)h * nb + i] : 1.0f;
 
     stage_load(0);
     stage_write(0);
@@ -171,43 +175,68 @@ __global__ __launch_bounds__(64 * (B / 32), 2) void quest_score_kernel(QuestArgs
     for (int c = 0; c < nch; ++c) {
       const int cur = c & 1;
       if (c + 1 < nch) stage_load(c + 1);
-      // bf16 bounds: two accumulators (even and odd contraction steps), independent
-      // product chains; the split bounds' longer contraction keeps one (and the
-      // occupancy its registers allow)
+      // bf16 bounds: two accumulators per head (even and odd contraction steps),
+      // independent product chains; the split bounds' longer contraction keeps one
       constexpr int NA = NP == 2 ? 2 : 1;
-      f32x16 accs[NA];
+      f32x16 accs[HP][NA];
 #pragma unroll
-      for (int q = 0; q < NA; ++q) accs[q] = f32x16{0};
+      for (int hp = 0; hp < HP; ++hp)
+#pragma unroll
+        for (int q = 0; q < NA; ++q) accs[hp][q] = f32x16{0};
       const unsigned char* bb = lds + cur * C::BUF + (l & 31) * C::LROW + 16 * (l >> 5);
 #pragma unroll
       for (int s = 0; s < C::KSTEPS; ++s) {
         const u32x4 bf = *(const u32x4*)(bb + 32 * s);
-        const u32x4 af = ((s / C::NS) & 1) ? qn[s % C::NS] : qp[s % C::NS];
-        accs[s % NA] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af),
-                                                               __builtin_bit_cast(bf16x8, bf),
-                                                               accs[s % NA], 0, 0, 0);
-      }
-      f32x16 acc = accs[0];
 #pragma unroll
-      for (int q = 1; q < NA; ++q) acc += accs[q];
+        for (int hp = 0; hp < HP; ++hp) {
+          const u32x4 af = ((s / C::NS) & 1) ? qn[hp][s % C::NS] : qp[hp][s % C::NS];
+          accs[hp][s % NA] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, af), __builtin_bit_cast(bf16x8, bf), accs[hp][s % NA], 0,
+              0, 0);
+        }
+      }
       // maximum over this wave's valid rows, for column (block) 32c + (l & 31)
-      float m = -INFINITY;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int row = (e >> 2) * 8 + (l >> 5) * 4 + (e & 3);
-        if ((int64_t)i * B + wave * 32 + row < a.S) m = fmaxf(m, acc[e]);
+      for (int hp = 0; hp < HP; ++hp) {
+        f32x16 acc = accs[hp][0];
+#pragma unroll
+        for (int q = 1; q < NA; ++q) acc += accs[hp][q];
+        float m = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int row = (e >> 2) * 8 + (l >> 5) * 4 + (e & 3);
+          if ((int64_t)i * B + wave * 32 + row < a.S) m = fmaxf(m, acc[e]);
+        }
+        m = max_with_other_half(m);
+        if (l < 32) red[((cur * C::NW + wave) * HP + hp) * 32 + l] = m;
       }
-      m = max_with_other_half(m);
-      if (l < 32) red[(cur * C::NW + wave) * 32 + l] = m;
       if (c + 1 < nch) stage_write(cur ^ 1);
       __syncthreads();
-      if (wave == 0 && l < 32) {
-        const int j = c * C::CH + l;
-        if (j <= i) {
-          float v = red[cur * C::NW * 32 + l];
+      // wave hp (< HP) finishes head hp; a per-group row takes the maximum over
+      // all G heads: over the pass's heads through LDS, over passes in memory
+      const int j = c * C::CH + l;
+      if (wave < HP && l < 32 && j <= i) {
+        const int hp = wave;
+        float v = red[(cur * C::NW * HP + hp) * 32 + l];
 #pragma unroll
-          for (int w = 1; w < C::NW; ++w) v = fmaxf(v, red[(cur * C::NW + w) * 32 + l]);
-          v *= qs;
+        for (int w = 1; w < C::NW; ++w) v = fmaxf(v, red[((cur * C::NW + w) * HP + hp) * 32 + l]);
+        v *= qs[hp];
+        if (!a.per_group) {
+          a.scores[((size_t)(hbase + hx + hp) * nb + i) * nb + j] = v;
+        } else if (HP == 1) {
+          float* srow = a.scores + ((size_t)g * nb + i) * nb;
+          srow[j] = hx == 0 ? v : fmaxf(srow[j], v);
+        } else {
+          red[(2 * C::NW * HP + hp) * 32 + l] = v;
+        }
+      }
+      if (HP > 1 && a.per_group) {
+        __syncthreads();
+        if (wave == 0 && l < 32 && j <= i) {
+          float v = red[(2 * C::NW * HP) * 32 + l];
+#pragma unroll
+          for (int hp = 1; hp < HP; ++hp) v = fmaxf(v, red[(2 * C::NW * HP + hp) * 32 + l]);
+          float* srow = a.scores + ((size_t)g * nb + i) * nb;
           srow[j] = hx == 0 ? v : fmaxf(srow[j], v);
         }
       }
@@ -215,25 +244,33 @@ __global__ __launch_bounds__(64 * (B / 32), 2) void quest_score_kernel(QuestArgs
   }
 }
 
-template <int D, int B, bool FP8, int NP>
+template <int D, int B, bool FP8, int NP, int HP>
 hipError_t launch_quest_t(const Shape& sh, const QuestArgs& a, hipStream_t stream) {
   typedef QCfg<D, B, NP> C;
-  auto kern = quest_score_kernel<D, B, FP8, NP>;
-  static_assert(C::LDS_BYTES <= 80 * 1024, "LDS budget");
+  auto kern = quest_score_kernel<D, B, FP8, NP, HP>;
+  constexpr int lds_bytes = 2 * C::BUF + (2 * C::NW * HP + HP) * 32 * 4;
+  static_assert(lds_bytes <= 80 * 1024, "LDS budget");
   hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
   if (e != hipSuccess) return e;
-  const int Gu = sh.per_group ? 1 : sh.G();
+  const int Gu = sh.per_group ? 1 : sh.G() / HP;
   const int64_t rows8 = ((int64_t)sh.Hkv * sh.nb + 7) / 8;
-  hipLaunchKernelGGL(kern, dim3((unsigned)(rows8 * 8 * Gu)), dim3(C::NT), C::LDS_BYTES, stream,
-                     a);
+  hipLaunchKernelGGL(kern, dim3((unsigned)(rows8 * 8 * Gu)), dim3(C::NT), lds_bytes, stream, a);
   return hipGetLastError();
 }
 
 template <int D, int B>
 hipError_t launch_quest_db(const Shape& sh, const QuestArgs& a, hipStream_t stream) {
-  return sh.fp8 ? launch_quest_t<D, B, true, 4>(sh, a, stream)
-                : launch_quest_t<D, B, false, 2>(sh, a, stream);
+#ifndef BSA_QUEST_HP
+#define BSA_QUEST_HP 2
+#endif
+  // two heads per pass wherever the group size allows (at B = 64 the staging
+  // registers of the two-wave workgroup leave no room for the second head)
+  if (BSA_QUEST_HP == 2 && B == 128 && sh.G() % 2 == 0)
+    return sh.fp8 ? launch_quest_t<D, B, true, 4, 2>(sh, a, stream)
+                  : launch_quest_t<D, B, false, 2, 2>(sh, a, stream);
+  return sh.fp8 ? launch_quest_t<D, B, true, 4, 1>(sh, a, stream)
+                : launch_quest_t<D, B, false, 2, 1>(sh, a, stream);
 }
 
 }  // namespace
