@@ -70,7 +70,9 @@ def test_full_size_sampled_parity(cfg):
     print(f"[parity-full] {cfg.name} S={cfg.seq_len}", flush=True)
     inp = generate(cfg, "cuda")
     run = K.run_gpu(cfg, inp)
-    rep = K.check_all(cfg, inp, run, row_sample=48, unit_sample=24, score_sample=256)
+    # (the 1M layer's rows hold 8192 candidates each: fewer of them keep the test short)
+    rows = 192 if cfg.seq_len > 500000 else 512
+    rep = K.check_all(cfg, inp, run, row_sample=rows, unit_sample=128, score_sample=2048)
     print(f"  rows={rep.rows_checked} ambiguous={rep.ambiguous_rows} fired={rep.gate_fired} "
           f"max_abs={rep.max_abs:.3g} mean_abs={rep.mean_abs:.3g} lse={rep.lse_max:.3g}",
           flush=True)
