@@ -535,10 +535,12 @@ __global__ __launch_bounds__(256) void select_reg_kernel(SelArgs a) {
 
   RowKeys<SPL> sr, br;
   sr.cand_bits.clear();
-  // the row is read in chunks of up to 16 slots per lane, each chunk's loads issued
+  // the row is read in chunks of up to 32 slots per lane, each chunk's loads issued
   // together (indices clamped into the row, one wait per chunk) rather than one
   // load and one wait per slot
-  constexpr int CH = SPL <= 16 ? SPL : 8;
+  // (32 slots per chunk for the top-k-only forms, whose one wave per SIMD has the
+  // registers; 8 for the others)
+  constexpr int CH = SPL <= 16 ? SPL : (!FULL ? (SPL > 32 ? 32 : SPL) : 8);
 #pragma unroll
   for (int e0 = 0; e0 < SPL; e0 += CH) {
 #pragma unroll
