@@ -69,11 +69,35 @@ struct RowLoad<true> {  // 8 E4M3 codes
   static constexpr int elem_bytes = 1;
 };
 
-// Sum of `cnt` rows (stride row_stride elements) of 8 consecutive elements at base.
+// Query rows: one 16-byte load per row and thread, so 8 bf16 or 16 E4M3 codes.
 template <bool FP8>
+struct QLoad;
+
+template <>
+struct QLoad<false> : RowLoad<false> {
+  static constexpr int EPT = 8;
+};
+
+template <>
+struct QLoad<true> {  // 16 E4M3 codes
+  typedef u32x4 raw;
+  static constexpr int EPT = 16;
+  static constexpr int elem_bytes = 1;
+  static __device__ __forceinline__ raw load(const void* p) { return *(const u32x4*)p; }
+  static __device__ __forceinline__ void add(float* acc, const raw& v) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 x = e4m3x4_to_f32x4(v[q]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[4 * q + e] += x[e];
+    }
+  }
+};
+
+// Sum of `cnt` rows (row_bytes apart) of the elements one load of L covers at base.
+template <class L>
 __device__ __forceinline__ void sum_rows(const unsigned char* base, size_t row_bytes, int cnt,
                                          float* acc) {
-  typedef RowLoad<FP8> L;
   int t = 0;
   for (; t + 8 <= cnt; t += 8) {
     typename L::raw v[8];
@@ -85,11 +109,11 @@ __device__ __forceinline__ void sum_rows(const unsigned char* base, size_t row_b
   for (; t < cnt; ++t) L::add(acc, L::load(base + (size_t)t * row_bytes));
 }
 
-// Sum over the D/8 consecutive lanes that hold one head's row.
-template <int D>
+// Sum over the D/EPT consecutive lanes that hold one head's row.
+template <int D, int EPT>
 __device__ __forceinline__ float head_lane_sum(float x) {
 #pragma unroll
-  for (int o = D / 16; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  for (int o = D / (2 * EPT); o >= 1; o >>= 1) x += __shfl_xor(x, o);
   return x;
 }
 
@@ -98,36 +122,40 @@ __global__ void pool_q_kernel(const void* __restrict__ q, const float* __restric
                               float* __restrict__ qc, float* __restrict__ qn, int64_t S, int Hq,
                               int Hkv, int B, int nb, int per_group, int HW) {
   extern __shared__ float red[];  // [HW][D], per-head means for the group sum
-  typedef RowLoad<FP8> L;
+  typedef QLoad<FP8> L;
+  constexpr int EPT = L::EPT;
   const int i = blockIdx.x;
   const int h0 = blockIdx.y * HW;
   const int tid = threadIdx.x;
-  const int hl = (tid * 8) / D, d = (tid * 8) % D;
+  const int hl = (tid * EPT) / D, d = (tid * EPT) % D;
   const int h = h0 + hl;
   const bool active = h < Hq;
   const int64_t t0 = (int64_t)i * B;
   const int cnt = (int)((S - t0) < B ? (S - t0) : B);
-  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  float acc[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) acc[e] = 0.f;
   if (active) {
     const size_t row_bytes = (size_t)Hq * D * L::elem_bytes;
     const unsigned char* base = (const unsigned char*)q + (size_t)t0 * row_bytes +
                                 ((size_t)h * D + d) * L::elem_bytes;
-    sum_rows<FP8>(base, row_bytes, cnt, acc);
+    sum_rows<L>(base, row_bytes, cnt, acc);
   }
   const float mul = (FP8 && active ? q_scale[(size_t)h * nb + i] : 1.0f) / (float)cnt;
-  float mean[8];
+  float mean[EPT];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) mean[e] = acc[e] * mul;
+  for (int e = 0; e < EPT; ++e) mean[e] = acc[e] * mul;
 
   if (!per_group) {
     float ss = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) ss += mean[e] * mean[e];
-    ss = head_lane_sum<D>(ss);
+    for (int e = 0; e < EPT; ++e) ss += mean[e] * mean[e];
+    ss = head_lane_sum<D, EPT>(ss);
     if (active) {
       float* dst = qc + ((size_t)h * nb + i) * D + d;
-      *(f32x4*)dst = f32x4{mean[0], mean[1], mean[2], mean[3]};
-      *(f32x4*)(dst + 4) = f32x4{mean[4], mean[5], mean[6], mean[7]};
+#pragma unroll
+      for (int e = 0; e < EPT; e += 4)
+        *(f32x4*)(dst + e) = f32x4{mean[e], mean[e + 1], mean[e + 2], mean[e + 3]};
       if (qn && d == 0) qn[(size_t)h * nb + i] = sqrtf(ss);
     }
     return;
@@ -135,30 +163,33 @@ __global__ void pool_q_kernel(const void* __restrict__ q, const float* __restric
   // per-group rows: mean over the group's heads of the per-head means
   const int G = Hq / Hkv;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) red[hl * D + d + e] = mean[e];
+  for (int e = 0; e < EPT; ++e) red[hl * D + d + e] = mean[e];
   __syncthreads();
   const int ul = hl;  // this thread now works for local unit ul (if any)
   const int u = h0 / G + ul;
   const bool uact = ul < HW / G && u < Hkv;
-  float gm[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  float gm[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) gm[e] = 0.f;
   if (uact) {
     for (int gg = 0; gg < G; ++gg) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) gm[e] += red[(ul * G + gg) * D + d + e];
+      for (int e = 0; e < EPT; ++e) gm[e] += red[(ul * G + gg) * D + d + e];
     }
   }
   const float invg = 1.0f / (float)G;
   float ss = 0.f;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
+  for (int e = 0; e < EPT; ++e) {
     gm[e] *= invg;
     ss += gm[e] * gm[e];
   }
-  ss = head_lane_sum<D>(ss);
+  ss = head_lane_sum<D, EPT>(ss);
   if (uact) {
     float* dst = qc + ((size_t)u * nb + i) * D + d;
-    *(f32x4*)dst = f32x4{gm[0], gm[1], gm[2], gm[3]};
-    *(f32x4*)(dst + 4) = f32x4{gm[4], gm[5], gm[6], gm[7]};
+#pragma unroll
+    for (int e = 0; e < EPT; e += 4)
+      *(f32x4*)(dst + e) = f32x4{gm[e], gm[e + 1], gm[e + 2], gm[e + 3]};
     if (qn && d == 0) qn[(size_t)u * nb + i] = sqrtf(ss);
   }
 }
@@ -233,7 +264,7 @@ __global__ __launch_bounds__(64 * KW) void pool_k_kernel(
         pt += df * df;
       }
     }
-    pt = head_lane_sum<D>(pt);
+    pt = head_lane_sum<D, 8>(pt);
     mx = fmaxf(mx, pt);
   }
   pmax[w][l] = mx;
@@ -334,11 +365,12 @@ template <bool FP8, int D>
 hipError_t launch_pool_t(const Shape& sh, const void* q, const void* k, const float* q_scale,
                          const float* k_scale, float* q_centroid, float* q_norm,
                          float* k_centroid, float* k_radius, hipStream_t stream) {
-  const int maxh = 2048 / D;  // heads per workgroup at 256 threads
+  constexpr int EPT = QLoad<FP8>::EPT;
+  const int maxh = 256 * EPT / D;  // heads per workgroup at 256 threads
   int HW = sh.Hq < maxh ? sh.Hq : maxh;
   if (sh.per_group) HW = (HW / sh.G()) * sh.G();  // whole groups per workgroup
   dim3 gq(sh.nb, (sh.Hq + HW - 1) / HW);
-  hipLaunchKernelGGL((pool_q_kernel<FP8, D>), gq, dim3(HW * D / 8), HW * D * sizeof(float), stream,
+  hipLaunchKernelGGL((pool_q_kernel<FP8, D>), gq, dim3(HW * D / EPT), HW * D * sizeof(float), stream,
                      q, q_scale, q_centroid, q_norm, sh.S, sh.Hq, sh.Hkv, sh.B, sh.nb,
                      sh.per_group, HW);
   hipError_t e = hipGetLastError();
