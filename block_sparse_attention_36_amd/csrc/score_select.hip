@@ -443,7 +443,7 @@ struct RowKeys {
 // candidate keep key 0, below every probe (x >= 1), so no candidacy test is needed.
 // Slots past the row (e >= nsl) hold key 0 as well, so the row is counted in
 // chunks of 8 slots behind one uniform branch each.  The widest forms (64 and 128
-// slots, one wave per SIMD) count per lane on the VALU and sum the lanes once;
+// slots, few waves per SIMD) count per lane on the VALU and sum the lanes once;
 // the others take a ballot popcount per slot on the scalar unit.
 template <int SPL>
 __device__ __forceinline__ int count_ge_reg(const RowKeys<SPL>& r, int nsl, unsigned x) {
@@ -514,8 +514,11 @@ __device__ void topk_reg(const RowKeys<SPL>& r, int nsl, int nc, int k, unsigned
 // FULL = false compiles the top-k and gate branches only (the rescue keys and the
 // mass probabilities would not fit in registers at 128 slots).  SIG compiles the
 // sigma gate's per-row part (its extra state stays out of the other forms).
+// (the 128-slot form is held to 256 registers, two waves per SIMD: alone on its
+// SIMD a wave waits out every load and reduction latency of its row)
 template <int SPL, bool FULL, bool SIG>
-__global__ __launch_bounds__(256) void select_reg_kernel(SelArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SPL >= 128 ? 2 : 1)))
+void select_reg_kernel(SelArgs a) {
   clear_overflow(a);
   const bool use_b = FULL && a.use_b, use_p = FULL && a.use_p;
   const int l = lane_id();
@@ -538,9 +541,9 @@ __global__ __launch_bounds__(256) void select_reg_kernel(SelArgs a) {
   // the row is read in chunks of up to 32 slots per lane, each chunk's loads issued
   // together (indices clamped into the row, one wait per chunk) rather than one
   // load and one wait per slot
-  // (32 slots per chunk for the top-k-only forms, whose one wave per SIMD has the
-  // registers; 8 for the others)
-  constexpr int CH = SPL <= 16 ? SPL : (!FULL ? (SPL > 32 ? 32 : SPL) : 8);
+  // (32 slots per chunk for the 32- and 64-slot top-k-only forms, 16 for the
+  // 128-slot one, whose 256 registers leave no room for more, 8 for the others)
+  constexpr int CH = SPL <= 16 ? SPL : (!FULL ? (SPL >= 128 ? 16 : SPL > 32 ? 32 : SPL) : 8);
 #pragma unroll
   for (int e0 = 0; e0 < SPL; e0 += CH) {
 #pragma unroll
