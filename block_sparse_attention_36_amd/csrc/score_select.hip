@@ -514,10 +514,12 @@ __device__ void topk_reg(const RowKeys<SPL>& r, int nsl, int nc, int k, unsigned
 // FULL = false compiles the top-k and gate branches only (the rescue keys and the
 // mass probabilities would not fit in registers at 128 slots).  SIG compiles the
 // sigma gate's per-row part (its extra state stays out of the other forms).
-// (the 128-slot form is held to 256 registers, two waves per SIMD: alone on its
-// SIMD a wave waits out every load and reduction latency of its row)
+// (the widest forms are held to the registers of two waves per SIMD, the 32-slot
+// form with every branch to three: a wave with its SIMD to itself waits out every
+// load and reduction latency of its row, and a few spilled registers cost less)
 template <int SPL, bool FULL, bool SIG>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SPL >= 128 ? 2 : 1)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
+    (SPL >= 128 || (SPL == 64 && FULL && !SIG)) ? 2 : (SPL == 32 && FULL) ? 3 : 1)))
 void select_reg_kernel(SelArgs a) {
   clear_overflow(a);
   const bool use_b = FULL && a.use_b, use_p = FULL && a.use_p;
