@@ -205,9 +205,10 @@ bsa_status bsa_score_select(const bsa_problem* problem, const bsa_select_params*
  * serving loops, harnesses that forbid hipMalloc).  It computes exactly what
  * bsa_score_select computes, with the same kernels and the same arguments
  * otherwise, but keeps its scratch (the score matrix when scores_out is NULL,
- * the kept-block masks and counts, the sigma gate's tile buffers, the overflow
- * word) in one fixed array of 64 MiB that the library holds on each GPU it runs
- * on until the process ends.  It calls no allocating routine.
+ * the kept-block masks and counts, the per-64-row count sums and offsets, the
+ * sigma gate's tile buffers, the overflow word) in one fixed array of 64 MiB
+ * that the library holds on each GPU it runs on until the process ends.  It
+ * calls no allocating routine.
  *
  *   Limit: a selection needing more than 64 MiB of scratch (that is
  *   bsa_score_select_workspace_size(problem, params, scores_out != NULL)) returns
