@@ -447,9 +447,10 @@ def summarize_pmc(fetch_dir: str, write_dir: str, out_json: str) -> int:
 
 
 def dense_context(bsa, torch, problem, cfg, inp, scale, out, lse, attn_ms: float,
-                  step_ms: float) -> dict:
+                  step_ms: float, v16=None) -> dict:
     """The same attention kernel on the full causal mask of the same problem (every
-    row keeps blocks 0..i): the dense prefill the sparse step stands against.
+    row keeps blocks 0..i): the dense prefill the sparse step stands against (for
+    E4M3 inputs on the same expanded V as the step, when it uses one).
     Context, not a target; run after the timed steps, so nothing here is timed in them."""
     dev = out.device
     nb, U = cfg.num_blocks, cfg.num_units
@@ -460,8 +461,14 @@ def dense_context(bsa, torch, problem, cfg, inp, scale, out, lse, attn_ms: float
     ci = (torch.arange(int(rp[-1]), device=dev, dtype=torch.int64) - rp[:-1][row_of]).to(torch.int32)
     rp = rp.to(torch.int32)
     del row_of
-    run = lambda: bsa.bsa_attention_fwd(problem, inp.q, inp.k, inp.v, rp, ci, scale, inp.q_scale,
-                                        inp.k_scale, inp.v_scale, out=out, lse=lse)
+    if v16 is not None:
+        run = lambda: bsa.bsa_attention_fwd_expanded_v(problem, inp.q, inp.k, v16, rp, ci, scale,
+                                                       inp.q_scale, inp.k_scale, inp.v_scale,
+                                                       out=out, lse=lse)
+    else:
+        run = lambda: bsa.bsa_attention_fwd(problem, inp.q, inp.k, inp.v, rp, ci, scale,
+                                            inp.q_scale, inp.k_scale, inp.v_scale, out=out,
+                                            lse=lse)
     run()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -719,7 +726,7 @@ def main(argv=None) -> int:
     if args.dense_context:
         print("[bench] dense causal attention (context)", file=sys.stderr, flush=True)
         res["dense_context"] = dense_context(bsa, torch, problem, cfg, inp, scale, out, lse,
-                                             attn_avg, ms_per_step)
+                                             attn_avg, ms_per_step, v16 if expand else None)
     if args.cpu_full:
         print("[bench] cpu baseline (oracle, whole workload)", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_full(cfg, inp)
