@@ -150,3 +150,15 @@ def test_cpu_full_runs_the_whole_tiny_workload():
     res = bench.cpu_full(cfg, inp)
     assert res["kind"] == "oracle" and res["value"] > 0 and res["cores"] >= 1
     assert res["cpu_model"] and res["affinity_cores"] >= 1
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The bench measures one GPU's share; asked for several it exits with a
+    message before touching a device."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "exactly one GPU" in r.stderr and r.stdout == ""
