@@ -38,10 +38,10 @@
 // codes are exact in fp32, so this is the bf16 result at twice the rate), with K
 // read raw from LDS and Q held raw in registers; V is expanded to bf16 in LDS
 // (exact) for O^T = V^T P^T.  q_scale and k_scale fold into the per-block logit
-// scale and v_scale into the probabilities.  When the caller has expanded the V
-// codes to bf16 beforehand (exactly, with the library's expansion kernel), the
-// V tiles are copied straight into LDS as bf16 and the per-block expansion and
-// its barrier drop out; the results are the same bit for bit.
+// scale and v_scale into the exponent of the probabilities.  When the caller has
+// expanded the V codes to bf16 beforehand (exactly, with the library's expansion
+// kernel), the V tiles are copied straight into LDS as bf16 and the per-block
+// expansion and its barrier drop out; the results are the same bit for bit.
 #include <atomic>
 
 #include "common.h"
@@ -490,8 +490,20 @@ __global__ __launch_bounds__(64 * (B / 32), 2) void attn_whole_kernel(AttnArgs a
     const float nref = m == -INFINITY ? 0.f : -m;
     float psum = 0.f;
     u32x4 pk[C::NKT][2];
+    if (FP8) {
+      // the block's value scale enters the exponent, p * vsc = 2^(x + log2 vsc), so
+      // the probabilities need no multiply and their sum is divided by vsc once; a
+      // zero scale (an all-zero block) is floored at 1e-30, whose products with the
+      // codes are negligible, and the sum still counts the block's keys
+      const float vs = fmaxf(vsc, 1e-30f);
+      const float nv = nref + __builtin_amdgcn_logf(vs);
 #pragma unroll
-    for (int kt2 = 0; kt2 < C::NKT; ++kt2) probs(s[kt2], nref, sl, vsc, psum, pk[kt2]);
+      for (int kt2 = 0; kt2 < C::NKT; ++kt2) probs(s[kt2], nv, sl, 1.0f, psum, pk[kt2]);
+      psum *= __builtin_amdgcn_rcpf(vs);
+    } else {
+#pragma unroll
+      for (int kt2 = 0; kt2 < C::NKT; ++kt2) probs(s[kt2], nref, sl, vsc, psum, pk[kt2]);
+    }
     lsum += psum;
 
     // ---- V(n) has landed everywhere and K(n) is free: request K(n + 1)
