@@ -396,13 +396,14 @@ def _pmc_rows(d: str, counter: str):
 ATTN_KERNEL = "attn_whole_kernel"
 
 
-# How the counter record is made (run from /tmp with TMPDIR=/tmp; $R is the repository).
+# How the counter record is made (run from /tmp with TMPDIR=/tmp; $R is the repository,
+# $OUT the folder the profiler writes to).
 PMC_COMMANDS = [
     "rocprofv3 --pmc {c} --kernel-include-regex \"attn_|pool_|select_|score_|copy|scan_|compact_|run_sum_\" "
-    "--output-format csv -d $R/gpurun_out/pmc_{d} -o run -- python3 $R/bench.py --steps 1 --warmup 1 "
+    "--output-format csv -d $OUT/pmc_{d} -o run -- python3 $R/bench.py --steps 1 --warmup 1 "
     "--no-cpu-baseline --calibrate-copy".format(c=c, d=d)
     for c, d in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write"))
-] + ["python3 $R/bench.py --summarize-pmc $R/gpurun_out/pmc_fetch $R/gpurun_out/pmc_write "
+] + ["python3 $R/bench.py --summarize-pmc $OUT/pmc_fetch $OUT/pmc_write "
      "$R/profiles/attention_dual128k_counters.json"]
 
 
