@@ -1,6 +1,7 @@
-"""The C ABI checks of test_abi.py, run against the sanitized build of the host
-layer: api.cpp compiled by g++ with AddressSanitizer and UndefinedBehaviorSanitizer
-(every validation, sizing and error path the tests drive), in a child process
+"""The C ABI checks of test_abi.py and test_abi_fuzz.py, run against the sanitized
+build of the host layer: api.cpp compiled by g++ with AddressSanitizer and
+UndefinedBehaviorSanitizer (every validation, sizing and error path the tests
+drive), in a child process
 with the ASan runtime preloaded.  CPU only."""
 
 import os
@@ -48,7 +49,8 @@ def test_sanitized_library_is_the_one_loaded(sanitized_env):
 def test_abi_checks_pass_under_asan_and_ubsan(sanitized_env):
     env, _ = sanitized_env
     out = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
-                          os.path.join(ROOT, "tests", "test_abi.py")],
+                          os.path.join(ROOT, "tests", "test_abi.py"),
+                          os.path.join(ROOT, "tests", "test_abi_fuzz.py")],
                          cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert out.returncode == 0, (out.stdout[-3000:] + out.stderr[-3000:])
     assert "passed" in out.stdout and "ERROR: AddressSanitizer" not in out.stderr
