@@ -1,8 +1,7 @@
 """The C ABI checks of test_abi.py and test_abi_fuzz.py, run against the sanitized
 build of the host layer: api.cpp compiled by g++ with AddressSanitizer and
 UndefinedBehaviorSanitizer (every validation, sizing and error path the tests
-drive), in a child process
-with the ASan runtime preloaded.  CPU only."""
+drive), in a child process with the ASan runtime preloaded.  CPU only."""
 
 import os
 import shutil
