@@ -10,14 +10,17 @@ import torch
 
 import bsa_check as K
 from oracle import bsa_oracle as O
+from random_layers import random_layers
 from workloads import config_by_name, generate, scaled
 
 
 def _oracle_run(cfg, inp):
     """A GpuRun-shaped record computed by the oracle (fp32 where the library
-    exports fp32, selection re-run on the fp32 scores as the harness does)."""
+    exports fp32, selection re-run on the fp32 scores and bounds as the harness does)."""
+    scales = [None if x is None else x.cpu().numpy() for x in (inp.q_scale, inp.k_scale,
+                                                               inp.v_scale)]
     Q, Kk, V = O.decode_inputs(*(K._raw(t) for t in (inp.q, inp.k, inp.v)), cfg.dtype,
-                               cfg.block_size)
+                               cfg.block_size, *scales)
     qbar, qn = O.pool_queries(Q, cfg.block_size, cfg.num_kv_heads, cfg.granularity)
     kbar, kr = O.pool_keys(Kk, cfg.block_size)
     kmin, kmax = O.key_block_bounds(Kk, cfg.block_size)
@@ -27,13 +30,21 @@ def _oracle_run(cfg, inp):
         s = O.block_scores(qbar, kbar, cfg.num_q_heads, cfg.num_kv_heads, cfg.granularity)
     s32 = np.nan_to_num(s).astype(np.float32)
     p = K.params_of(cfg)
-    kept, fired = O.select(s32.astype(np.float64), None, p)
+    b32 = None
+    if cfg.rescue_fraction > 0:
+        b = O.rescue_bounds(s32.astype(np.float64), np.asarray(qn, np.float32).astype(np.float64),
+                            np.asarray(kr, np.float32).astype(np.float64), cfg.num_q_heads,
+                            cfg.num_kv_heads, cfg.granularity)
+        b32 = np.nan_to_num(b).astype(np.float32)
+    kept, fired = O.select(s32.astype(np.float64),
+                           None if b32 is None else b32.astype(np.float64), p)
     rp, ci = O.to_csr(kept)
     out, lse = O.attention(Q, Kk, V, kept, cfg.block_size, 1 / math.sqrt(cfg.head_dim),
                            cfg.granularity)
     f32 = lambda a: torch.from_numpy(np.asarray(a, dtype=np.float32))  # noqa: E731
     return K.GpuRun(torch.from_numpy(out).to(torch.bfloat16), f32(lse), rp, ci, f32(qbar),
-                    f32(qn), f32(kbar), f32(kr), torch.from_numpy(s32), None,
+                    f32(qn), f32(kbar), f32(kr), torch.from_numpy(s32),
+                    None if b32 is None else torch.from_numpy(b32),
                     fired.reshape(-1).astype(np.uint8), f32(kmin), f32(kmax))
 
 
@@ -98,3 +109,14 @@ def test_harness_accepts_oracle_quest_results_and_rejects_a_wrong_bound(gran):
     sc[0, 7, 2] *= 1.01
     with pytest.raises(AssertionError, match="quest score"):
         K.check_all(cfg, inp, K.GpuRun(**{**run.__dict__, "scores": sc}))
+
+
+@pytest.mark.parametrize("cfg", random_layers(16), ids=lambda c: c.name)
+def test_harness_accepts_oracle_results_on_the_random_layers(cfg):
+    """Every random layer the GPU parity test runs is decidable by the checker: the
+    oracle's own results pass in full with no row or tile left in doubt."""
+    inp = generate(cfg, "cpu")
+    rep = K.check_all(cfg, inp, _oracle_run(cfg, inp))
+    assert rep.rows_checked == cfg.num_units * cfg.num_blocks
+    assert rep.ambiguous_rows == 0 and rep.ambiguous_tiles == 0
+    assert rep.max_abs < 2e-2
