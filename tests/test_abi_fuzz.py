@@ -179,3 +179,37 @@ def test_non_finite_scales_and_thresholds_never_pass_validation(lib):
             s = bsa.make_params(top_k=4, gate=gate, gate_threshold=0.05, gate_factor=2)
             s.gate_threshold = v
             assert lib.bsa_csr_capacity_bound(P, ctypes.byref(s)) == -1, (gate, v)
+
+
+def test_last_error_is_per_thread(lib):
+    """Threads that fail in different ways each read back their own reason."""
+    import threading
+
+    reasons = {}
+    barrier = threading.Barrier(4)
+
+    def worker(t):
+        p = bsa.Problem(seq_len=4096, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                        block_size=128, dtype=0, granularity=0)
+        if t == 0:
+            p.head_dim = 96
+        elif t == 1:
+            p.num_q_heads = 6
+            p.num_kv_heads = 4
+        elif t == 2:
+            p.dtype = 7
+        # (thread 3 keeps a valid problem: it fails on the missing buffers)
+        P = ctypes.byref(p)
+        barrier.wait()
+        for _ in range(200):
+            st = lib.bsa_pool(P, *([None] * 9))
+            reasons.setdefault(t, set()).add((st, lib.bsa_last_error()))
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(4)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    for t in range(4):
+        assert len(reasons[t]) == 1, (t, reasons[t])  # the same reason on every call
+    assert len({next(iter(reasons[t]))[1] for t in range(4)}) == 4  # and four different ones
