@@ -324,7 +324,7 @@ def test_expanded_v_attention_equals_the_codes_path(cfg):
     assert torch.equal(lse0, lse1)
 
 
-RANDOM = random_layers(16)
+RANDOM = random_layers(48)
 
 
 @pytest.mark.parametrize("cfg", RANDOM, ids=[c.name for c in RANDOM])

@@ -111,7 +111,7 @@ def test_harness_accepts_oracle_quest_results_and_rejects_a_wrong_bound(gran):
         K.check_all(cfg, inp, K.GpuRun(**{**run.__dict__, "scores": sc}))
 
 
-@pytest.mark.parametrize("cfg", random_layers(16), ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", random_layers(48), ids=lambda c: c.name)
 def test_harness_accepts_oracle_results_on_the_random_layers(cfg):
     """Every random layer the GPU parity test runs is decidable by the checker: the
     oracle's own results pass in full with no row or tile left in doubt."""
