@@ -51,7 +51,11 @@
  *
  *   Streams: hip_stream is a hipStream_t passed as void* (NULL = null stream).
  *   After host-side validation each call enqueues its kernels on that stream and
- *   returns; results are ready when the stream reaches that point.
+ *   returns; results are ready when the stream reaches that point.  A call makes
+ *   no allocation, copy, memset or synchronisation, so a sequence of calls may be
+ *   captured into a HIP graph once each has run eagerly on that device (the first
+ *   call per device raises kernel LDS limits and, for bsa_score_select_noalloc,
+ *   looks up its scratch address).
  *
  *   Errors: arguments are validated on the host before anything is launched; a
  *   failing call launches nothing and returns a non-zero bsa_status, with a
