@@ -26,6 +26,8 @@
 // Workgroups go kv-head major, the longest tiles first, and the units of one kv
 // head at one tile on one XCD (workgroup id mod 8), whose L2 then holds their
 // common bounds.
+#include <atomic>
+
 #include "common.h"
 #include "launch.h"
 
@@ -250,9 +252,17 @@ hipError_t launch_quest_t(const Shape& sh, const QuestArgs& a, hipStream_t strea
   auto kern = quest_score_kernel<D, B, FP8, NP, HP>;
   constexpr int lds_bytes = 2 * C::BUF + (2 * C::NW * HP + HP) * 32 * 4;
   static_assert(lds_bytes <= 80 * 1024, "LDS budget");
-  hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
-  if (e != hipSuccess) return e;
+  // the LDS limit is raised once per device (64 KiB and more need the attribute)
+  static std::atomic<uint64_t> attr_set{0};
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  const uint64_t bit = 1ull << (dev & 63);
+  if (!(attr_set.load(std::memory_order_acquire) & bit)) {
+    const hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+    if (e != hipSuccess) return e;
+    attr_set.fetch_or(bit, std::memory_order_acq_rel);
+  }
   const int Gu = sh.per_group ? 1 : sh.G() / HP;
   const int64_t rows8 = ((int64_t)sh.Hkv * sh.nb + 7) / 8;
   hipLaunchKernelGGL(kern, dim3((unsigned)(rows8 * 8 * Gu)), dim3(C::NT), lds_bytes, stream, a);

@@ -18,7 +18,10 @@ pytestmark = pytest.mark.gpu
 
 CASES = [scaled(config_by_name("gqa32k"), 4096 + 77, num_q_heads=8, num_kv_heads=2),
          scaled(config_by_name("dual128k"), 4096 + 100, num_q_heads=8, num_kv_heads=2),
-         scaled(config_by_name("msa1m"), 4096 + 70, num_q_heads=8, num_kv_heads=2)]
+         scaled(config_by_name("msa1m"), 4096 + 70, num_q_heads=8, num_kv_heads=2),
+         scaled(config_by_name("quest64k"), 4096 + 5, num_q_heads=8, num_kv_heads=2),
+         scaled(config_by_name("sigma64k"), 4096 + 33, num_q_heads=8, num_kv_heads=2,
+                name="padded-sigma64k")]
 
 
 def _gpu_or_skip():
@@ -27,16 +30,25 @@ def _gpu_or_skip():
 
 
 class Layer:
-    """One layer's inputs and preallocated outputs; run() enqueues pool, selection
-    and attention on the current stream without allocating."""
+    """One layer's inputs and preallocated outputs; run() enqueues the layer's calls
+    (pool or key bounds, selection in CSR or padded form, attention) on the current
+    stream without allocating."""
 
     def __init__(self, cfg, inp, noalloc):
         import bsa_check as K
         self.cfg, self.inp, self.noalloc = cfg, inp, noalloc
+        self.quest = cfg.backbone == "quest"
+        self.padded = cfg.name.startswith("padded")
         self.problem = bsa.make_problem(inp.q, inp.k, cfg.block_size, K.granularity_code(cfg))
         self.params = K.lib_params(cfg)
-        self.pool = bsa.bsa_pool(self.problem, inp.q, inp.k, inp.q_scale, inp.k_scale)
-        self.bufs = bsa.SelectBuffers(self.problem, self.params, "cuda")
+        if self.quest:
+            self.kb = bsa.bsa_pool_key_bounds(self.problem, inp.k, inp.k_scale)
+            self.qbufs = bsa.QuestBuffers(self.problem, "cuda")
+        else:
+            self.pool = bsa.bsa_pool(self.problem, inp.q, inp.k, inp.q_scale, inp.k_scale)
+        if self.padded:
+            self.pbufs = bsa.PaddedBuffers(self.problem, self.params, "cuda")
+        self.bufs = bsa.SelectBuffers(self.problem, self.params, "cuda", given_scores=self.quest)
         S, Hq, D = inp.q.shape
         self.out = torch.empty(S, Hq, D, dtype=torch.bfloat16, device="cuda")
         self.lse = torch.empty(Hq, S, dtype=torch.float32, device="cuda")
@@ -45,10 +57,21 @@ class Layer:
 
     def run(self):
         i, p = self.inp, self.problem
-        bsa.bsa_pool(p, i.q, i.k, i.q_scale, i.k_scale, out=self.pool)
-        select = bsa.bsa_score_select_noalloc if self.noalloc else bsa.bsa_score_select
-        sel = select(p, self.params, self.pool, buffers=self.bufs)
         scale = 1.0 / math.sqrt(self.cfg.head_dim)
+        if self.quest:
+            bsa.bsa_pool_key_bounds(p, i.k, i.k_scale, out=self.kb)
+            sc = bsa.bsa_quest_scores(p, i.q, self.kb[0], self.kb[1], i.q_scale,
+                                      buffers=self.qbufs)
+            sel = bsa.bsa_select_scores(p, self.params, sc, buffers=self.bufs)
+        else:
+            bsa.bsa_pool(p, i.q, i.k, i.q_scale, i.k_scale, out=self.pool)
+            if self.padded:
+                pl = bsa.bsa_score_select_padded(p, self.params, self.pool, buffers=self.pbufs)
+                bsa.bsa_attention_fwd_padded(p, i.q, i.k, i.v, pl.kv_idx, scale, i.q_scale,
+                                             i.k_scale, i.v_scale, out=self.out, lse=self.lse)
+                return
+            select = bsa.bsa_score_select_noalloc if self.noalloc else bsa.bsa_score_select
+            sel = select(p, self.params, self.pool, buffers=self.bufs)
         if self.v16 is not None:
             bsa.bsa_expand_e4m3(p, i.v, out=self.v16)
             bsa.bsa_attention_fwd_expanded_v(p, i.q, i.k, self.v16, sel.row_ptr, sel.col_idx,
@@ -59,9 +82,15 @@ class Layer:
                                   i.k_scale, i.v_scale, out=self.out, lse=self.lse)
 
     def snapshot(self):
-        nnz = int(self.bufs.row_ptr[-1].item())
-        return (self.bufs.row_ptr.clone(), self.bufs.col_idx[:nnz].clone(),
-                self.out.view(torch.int16).clone(), self.lse.clone())
+        if self.padded:
+            lists = (self.pbufs.kv_idx.clone(),)
+        else:
+            nnz = int(self.bufs.row_ptr[-1].item())
+            lists = (self.bufs.row_ptr.clone(), self.bufs.col_idx[:nnz].clone())
+        return lists + (self.out.view(torch.int16).clone(), self.lse.clone())
+
+    def clear_lists(self):
+        (self.pbufs.kv_idx if self.padded else self.bufs.col_idx).zero_()
 
 
 def _same(a, b):
@@ -107,7 +136,7 @@ def test_graph_replays_match_eager(cfg):
         # outputs cleared between replays, so each replay is seen to write them again
         captured.out.zero_()
         captured.lse.zero_()
-        captured.bufs.col_idx.zero_()
+        captured.clear_lists()
         graph.replay()
         torch.cuda.synchronize()
         assert _same(ref, captured.snapshot()), f"replay {replay}"
