@@ -235,10 +235,14 @@ __global__ __launch_bounds__(256) void select_kernel(SelArgs a) {
   clear_overflow(a);
   const int l = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int row = blockIdx.x * (blockDim.x >> 6) + wave;
-  if (row >= a.rows) return;  // no workgroup barriers below
+  const int w = blockIdx.x * (blockDim.x >> 6) + wave;
+  if (w >= a.rows) return;  // no workgroup barriers below
   const int nb = a.nb;
-  const int u = row / nb, i = row % nb;
+  // longest rows first: wave w takes query block nb - 1 - w / U of unit w % U, so
+  // the last workgroups dispatched hold the shortest rows
+  const int U = a.rows / nb;
+  const int u = w % U, i = nb - 1 - w / U;
+  const int row = u * nb + i;
   const int g = a.per_group ? u : u / a.G;
   float* s = sm + (size_t)wave * a.per_wave_floats;
   float* b = s + a.nw * 64;
@@ -529,7 +533,9 @@ void select_reg_kernel(SelArgs a) {
   const int r = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nb = a.nb;
   if (r >= a.units * a.ni) return;  // no workgroup barriers below
-  const int u = r / a.ni, i = a.i0 + r % a.ni;
+  // longest rows first: query block i0 + ni - 1 - r / units of unit r % units, so
+  // the last workgroups dispatched hold the shortest rows
+  const int u = r % a.units, i = a.i0 + a.ni - 1 - r / a.units;
   const int row = u * nb + i;
   const int g = a.per_group ? u : u / a.G;
   const int sink = a.force_sink;
