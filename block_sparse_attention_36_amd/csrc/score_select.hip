@@ -2,9 +2,10 @@
 //
 // Scores: s[u][i][j] = qbar[u][i] . kbar[kv(u)][j], j <= i, the mean-pooling inner
 // product ("Uncertainty-gated selection for block-sparse attention", technical
-// summary, Methodology step 1).  Computed on the fp32 matrix cores
-// (V_MFMA_F32_32X32X2_F32), one workgroup per 64x64 tile of the causal lower
-// triangle, so the scores keep full fp32 accuracy.
+// summary, Methodology step 1).  Computed on the bf16 matrix cores with each fp32
+// operand split into two bf16 parts (three products per step), one workgroup per
+// 128x128 tile of the causal lower triangle, to within about 3e-6 of
+// ||qbar|| ||kbar||.
 //
 // Selection (one wave per row (u, i)), on the candidates C_i = {0..i} minus the
 // forced blocks, ranked by descending score with the lowest index first on ties:
@@ -45,16 +46,33 @@ namespace {
 
 // One workgroup of four waves per 128 x 128 tile of the causal lower triangle;
 // wave w computes the 64 x 64 sub-tile (w / 2, w % 2) as 2 x 2 products of 32 x 32,
-// so every operand read from LDS feeds two products.  The tile's 128 query and
-// 128 key centroids are staged through LDS 32 dimensions at a time with
-// coalesced 16-byte loads; rows are padded to 33 floats so the per-lane operand
-// reads of one product (32 rows, one column) hit distinct banks.  Each score is
-// accumulated over the dimensions in ascending pairs, one V_MFMA_F32_32X32X2_F32
-// step per pair.  The grid enumerates the lower-triangle tiles only (tile t of
-// row it = the largest with it(it+1)/2 <= t), so consecutive workgroups, which
-// the dispatcher deals round-robin to the eight XCDs, spread the work evenly; a
-// square grid with the upper tiles exiting would give XCD k only the tile rows
-// it = k (mod 8).
+// so every operand read from LDS feeds two products.  The products run on the
+// bf16 matrix cores (V_MFMA_F32_32X32X16_BF16) with each fp32 centroid split into
+// a bf16 head and a bf16 remainder, x = hi + lo with |x - hi - lo| <= 2^-18 |x|,
+// and three products per step, hi*hi + hi*lo + lo*hi (the dropped lo*lo is below
+// 2^-18 of |q_d k_d|), accumulated in fp32: every score is within about 3e-6 of
+// ||qbar|| ||kbar|| of the exact one, at three sixteenths of the fp32 matrix-core
+// cost.  The tile's 128 query and 128 key centroids are staged through LDS 32
+// dimensions at a time with coalesced 16-byte loads (the next 32 loaded into
+// registers while the current ones are multiplied), split as they are stored;
+// a staged row holds its 32 heads then its 32 remainders and is padded to 144
+// bytes (9 x 16), so the 16-byte operand reads of 16 consecutive rows fall on 16
+// different 16-byte bank groups.  The grid enumerates the lower-triangle tiles
+// only (tile t of row it = the largest with it(it+1)/2 <= t), so consecutive
+// workgroups, which the dispatcher deals round-robin to the eight XCDs, spread
+// the work evenly; a square grid with the upper tiles exiting would give XCD k
+// only the tile rows it = k (mod 8).
+__device__ __forceinline__ void split_bf16x4(const f32x4& x, u32x2& hi, u32x2& lo) {
+  hi = u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+  const float r0 = x[0] - __uint_as_float(hi[0] << 16);
+  const float r1 = x[1] - __uint_as_float(hi[0] & 0xFFFF0000u);
+  const float r2 = x[2] - __uint_as_float(hi[1] << 16);
+  const float r3 = x[3] - __uint_as_float(hi[1] & 0xFFFF0000u);
+  lo = u32x2{pack_bf16x2(r0, r1), pack_bf16x2(r2, r3)};
+}
+
+constexpr int kScoreRow = 144;  // bytes per staged row: 32 bf16 heads, 32 remainders, pad
+
 __global__ __launch_bounds__(256) void score_kernel(const float* __restrict__ qc,
                                                     const float* __restrict__ kc,
                                                     float* __restrict__ scores, int nb, int D,
@@ -64,7 +82,7 @@ __global__ __launch_bounds__(256) void score_kernel(const float* __restrict__ qc
   while ((it + 1) * (it + 2) / 2 <= t) ++it;  // float rounding, either way
   while (it * (it + 1) / 2 > t) --it;
   const int jt = t - it * (it + 1) / 2;
-  __shared__ float As[128 * 33], Bs[128 * 33];
+  __shared__ __attribute__((aligned(16))) unsigned char As[128 * kScoreRow], Bs[128 * kScoreRow];
   const int tid = threadIdx.x, l = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wi = w >> 1, wj = w & 1, hf = l >> 5;
   const int g = per_group ? u : u / G;
@@ -73,8 +91,6 @@ __global__ __launch_bounds__(256) void score_kernel(const float* __restrict__ qc
   for (int x = 0; x < 2; ++x)
 #pragma unroll
     for (int y = 0; y < 2; ++y) acc[x][y] = f32x16{0};
-  // the next 32 dimensions are loaded into registers while the current ones
-  // are multiplied
   f32x4 av[4], bv[4];
   auto load = [&](int k0) {
 #pragma unroll
@@ -90,26 +106,38 @@ __global__ __launch_bounds__(256) void score_kernel(const float* __restrict__ qc
 #pragma unroll
     for (int t4 = 0; t4 < 4; ++t4) {
       const int idx = tid + 256 * t4, row = idx >> 3, c4 = (idx & 7) * 4;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        As[row * 33 + c4 + e] = av[t4][e];
-        Bs[row * 33 + c4 + e] = bv[t4][e];
-      }
+      u32x2 h, r;
+      split_bf16x4(av[t4], h, r);
+      *(u32x2*)(As + row * kScoreRow + c4 * 2) = h;
+      *(u32x2*)(As + row * kScoreRow + 64 + c4 * 2) = r;
+      split_bf16x4(bv[t4], h, r);
+      *(u32x2*)(Bs + row * kScoreRow + c4 * 2) = h;
+      *(u32x2*)(Bs + row * kScoreRow + 64 + c4 * 2) = r;
     }
     __syncthreads();
     if (k0 + 32 < D) load(k0 + 32);
-    // A: rows wi*64 + 32x + l%32, B: columns wj*64 + 32y + l%32; lane half hf
-    // takes k = 2s + hf of step s
-    const float* ar = As + (wi * 64 + (l & 31)) * 33 + hf;
-    const float* br = Bs + (wj * 64 + (l & 31)) * 33 + hf;
+    // A: query rows wi*64 + 32x + l%32, B: key rows wj*64 + 32y + l%32; lane half
+    // hf takes dimensions 8hf..8hf+7 of each 16-dimension step s
+    const unsigned char* ar = As + (wi * 64 + (l & 31)) * kScoreRow + hf * 16;
+    const unsigned char* br = Bs + (wj * 64 + (l & 31)) * kScoreRow + hf * 16;
 #pragma unroll
-    for (int st = 0; st < 16; ++st) {
-      const float a0 = ar[2 * st], a1 = ar[32 * 33 + 2 * st];
-      const float b0 = br[2 * st], b1 = br[32 * 33 + 2 * st];
-      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0][0], 0, 0, 0);
-      acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc[0][1], 0, 0, 0);
-      acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
-      acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
+    for (int s = 0; s < 2; ++s) {
+      bf16x8 ah[2], al[2], bh[2], bl[2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        ah[x] = *(const bf16x8*)(ar + x * 32 * kScoreRow + s * 32);
+        al[x] = *(const bf16x8*)(ar + x * 32 * kScoreRow + 64 + s * 32);
+        bh[x] = *(const bf16x8*)(br + x * 32 * kScoreRow + s * 32);
+        bl[x] = *(const bf16x8*)(br + x * 32 * kScoreRow + 64 + s * 32);
+      }
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y) {
+          acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[x], bl[y], acc[x][y], 0, 0, 0);
+          acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[x], bh[y], acc[x][y], 0, 0, 0);
+          acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[x], bh[y], acc[x][y], 0, 0, 0);
+        }
     }
     __syncthreads();
   }
