@@ -289,6 +289,47 @@ def test_repeat_runs_are_bitwise_identical():
 
 # E4M3 shapes (every (head_dim, block_size) pair, ragged tails, both granularities)
 # and the 1M workload at full size for the expanded-V attention
+# the score kernel's own arithmetic: bf16 products of fp32 centroids split into two
+# bf16 parts each, against float64 products of the same centroids
+SCORE_ERR = [scaled(config_by_name("gqa32k"), 4096 + 77, num_q_heads=8, num_kv_heads=2,
+                    name="scores-D128"),
+             scaled(config_by_name("gqa32k"), 4096 + 77, num_q_heads=8, num_kv_heads=2,
+                    head_dim=64, block_size=64, name="scores-D64"),
+             scaled(config_by_name("msa1m"), 8192 + 1, num_q_heads=16, num_kv_heads=2,
+                    name="scores-group-fp8")]
+
+
+@pytest.mark.parametrize("cfg", SCORE_ERR, ids=[c.name for c in SCORE_ERR])
+def test_score_kernel_error_bound(cfg):
+    """Every exported score within 1e-5 * ||qbar|| * ||kbar|| of the float64 product of
+    the centroids the library itself pooled (the split operands carry about 2^-17 of
+    each product; the parity bound against the oracle is 1e-4)."""
+    _gpu_or_skip()
+    import block_sparse_attention_36_amd as bsa
+    import bsa_check as K
+    print(f"[scores] {cfg.name} S={cfg.seq_len}", flush=True)
+    inp = generate(cfg, "cpu").to("cuda")
+    problem = bsa.make_problem(inp.q, inp.k, cfg.block_size, K.granularity_code(cfg))
+    pool = bsa.bsa_pool(problem, inp.q, inp.k, inp.q_scale, inp.k_scale)
+    sel = bsa.bsa_score_select(problem, K.lib_params(cfg), pool, export=True)
+    torch.cuda.synchronize()
+    qc = pool.q_centroid.double().cpu()
+    kc = pool.k_centroid.double().cpu()
+    s = sel.scores.double().cpu()
+    U, nb = qc.shape[0], qc.shape[1]
+    G = 1 if cfg.granularity == "group" else cfg.num_q_heads // cfg.num_kv_heads
+    tri = torch.tril(torch.ones(nb, nb, dtype=torch.bool))
+    worst = 0.0
+    for u in range(U):
+        g = u if cfg.granularity == "group" else u // G
+        exact = qc[u] @ kc[g].T
+        norm = qc[u].norm(dim=1)[:, None] * kc[g].norm(dim=1)[None, :] + 1e-30
+        err = ((s[u] - exact).abs() / norm)[tri]
+        worst = max(worst, float(err.max()))
+    print(f"  worst normwise score error {worst:.3g}", flush=True)
+    assert worst <= 1e-5
+
+
 EXPANDED_V = [c for c in SHAPES if c.dtype == "fp8"] + [
     scaled(config_by_name("dual128k_fp8"), 4096 + 77, num_q_heads=8, num_kv_heads=2),
     config_by_name("msa1m")]
