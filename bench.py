@@ -411,7 +411,7 @@ def summarize_pmc(fetch_dir: str, write_dir: str, out_json: str) -> int:
     """HBM bytes per attention launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
     each scaled by what the same counter reads for a plain copy of COPY_BYTES."""
     import statistics
-    out = {"kernel": "attn_whole_kernel<128, 128, false, false>", "workload": "dual128k",
+    out = {"kernel": "attn_whole_kernel<128, 128, false, false, false>", "workload": "dual128k",
            "kernel_source_hash": source_hash("attention.hip", "common.h"),
            "commands": PMC_COMMANDS}
     others = {}
@@ -448,10 +448,10 @@ def summarize_pmc(fetch_dir: str, write_dir: str, out_json: str) -> int:
 
 
 def dense_context(bsa, torch, problem, cfg, inp, scale, out, lse, attn_ms: float,
-                  step_ms: float, v16=None) -> dict:
+                  step_ms: float, v16=None, vprep=None) -> dict:
     """The same attention kernel on the full causal mask of the same problem (every
     row keeps blocks 0..i): the dense prefill the sparse step stands against (for
-    E4M3 inputs on the same expanded V as the step, when it uses one).
+    E4M3 inputs on the same expanded or prepared V as the step, when it uses one).
     Context, not a target; run after the timed steps, so nothing here is timed in them."""
     dev = out.device
     nb, U = cfg.num_blocks, cfg.num_units
@@ -462,7 +462,11 @@ def dense_context(bsa, torch, problem, cfg, inp, scale, out, lse, attn_ms: float
     ci = (torch.arange(int(rp[-1]), device=dev, dtype=torch.int64) - rp[:-1][row_of]).to(torch.int32)
     rp = rp.to(torch.int32)
     del row_of
-    if v16 is not None:
+    if vprep is not None:
+        run = lambda: bsa.bsa_attention_fwd_prepared_v(problem, inp.q, inp.k, vprep, rp, ci, scale,
+                                                       inp.q_scale, inp.k_scale, inp.v_scale,
+                                                       out=out, lse=lse)
+    elif v16 is not None:
         run = lambda: bsa.bsa_attention_fwd_expanded_v(problem, inp.q, inp.k, v16, rp, ci, scale,
                                                        inp.q_scale, inp.k_scale, inp.v_scale,
                                                        out=out, lse=lse)
@@ -558,8 +562,13 @@ def main(argv=None) -> int:
         bufs = bsa.SelectBuffers(problem, params, dev, export=False, given_scores=quest)
     # E4M3 V is expanded to its exact bf16 values inside each step (a lossless change
     # of format), and attention reads those; the padded-list path reads the codes
+    # (at head_dim = block_size = 128 into the transposed tiles the P V products read
+    # with one 16-byte LDS read per operand, bsa_prepare_v)
     expand = cfg.dtype == "fp8" and not padded
-    v16 = torch.empty(inp.v.shape, dtype=torch.bfloat16, device=dev) if expand else None
+    prepared = expand and cfg.head_dim == 128 and cfg.block_size == 128
+    v16 = (torch.empty(inp.v.shape, dtype=torch.bfloat16, device=dev)
+           if expand and not prepared else None)
+    vprep = bsa.bsa_prepare_v(problem, inp.v) if prepared else None
     out = torch.empty(cfg.seq_len, cfg.num_q_heads, cfg.head_dim, dtype=torch.bfloat16, device=dev)
     lse = torch.empty(cfg.num_q_heads, cfg.seq_len, dtype=torch.float32, device=dev)
     scale = 1.0 / math.sqrt(cfg.head_dim)
@@ -590,13 +599,19 @@ def main(argv=None) -> int:
             sel = bsa.bsa_score_select(problem, params, pool, buffers=bufs)
         if ev:
             ev[2].record()
-        if expand:
+        if prepared:
+            bsa.bsa_prepare_v(problem, inp.v, out=vprep)
+        elif expand:
             bsa.bsa_expand_e4m3(problem, inp.v, out=v16)
         if ev:
             ev[5].record()
         if padded:
             bsa.bsa_attention_fwd_padded(problem, inp.q, inp.k, inp.v, pbufs.kv_idx, scale,
                                          inp.q_scale, inp.k_scale, inp.v_scale, out=out, lse=lse)
+        elif prepared:
+            bsa.bsa_attention_fwd_prepared_v(problem, inp.q, inp.k, vprep, sel.row_ptr,
+                                             sel.col_idx, scale, inp.q_scale, inp.k_scale,
+                                             inp.v_scale, out=out, lse=lse)
         elif expand:
             bsa.bsa_attention_fwd_expanded_v(problem, inp.q, inp.k, v16, sel.row_ptr, sel.col_idx,
                                              scale, inp.q_scale, inp.k_scale, inp.v_scale,
@@ -673,11 +688,13 @@ def main(argv=None) -> int:
                      "frac_of_bf16_peak": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_from_profile(khash, cfg.name),
                      "kernel": f"{ATTN_KERNEL}<{cfg.head_dim},{cfg.block_size},"
-                               f"{str(cfg.dtype == 'fp8').lower()},{str(expand).lower()}>",
+                               f"{str(cfg.dtype == 'fp8').lower()},{str(expand).lower()},"
+                               f"{str(prepared).lower()}>",
                      "kernel_source_hash": khash},
         "stages_ms": {"pool": round(float(pool_ms.mean()), 4),
                       "score_select": round(float(sel_ms.mean()), 4),
-                      **({"expand_v": round(float(exp_ms.mean()), 4)} if expand else {}),
+                      **({"prepare_v" if prepared else "expand_v": round(float(exp_ms.mean()), 4)}
+                         if expand else {}),
                       "attention": round(attn_avg, 4)},
         "frac_of_bf16_peak_whole_step": round(kept_flops / (ms_per_step * 1e-3) / 1e12
                                               / PEAK_BF16_TFLOPS, 4),
@@ -727,7 +744,7 @@ def main(argv=None) -> int:
     if args.dense_context:
         print("[bench] dense causal attention (context)", file=sys.stderr, flush=True)
         res["dense_context"] = dense_context(bsa, torch, problem, cfg, inp, scale, out, lse,
-                                             attn_avg, ms_per_step, v16 if expand else None)
+                                             attn_avg, ms_per_step, v16, vprep)
     if args.cpu_full:
         print("[bench] cpu baseline (oracle, whole workload)", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_full(cfg, inp)

@@ -96,6 +96,9 @@ def load_library(path: str = LIB_PATH):
         "bsa_score_select_padded": ([PP, PS, P, P, P, P, P, P, I64, P, P, P, P, SZ, P],
                                     ctypes.c_int),
         "bsa_attention_fwd_padded": ([PP, P, P, P, P, P, P, P, I64, F, P, P, P], ctypes.c_int),
+        "bsa_prepared_v_bytes": ([PP], SZ),
+        "bsa_prepare_v": ([PP, P, P, P], ctypes.c_int),
+        "bsa_attention_fwd_prepared_v": ([PP, P, P, P, P, P, P, P, P, F, P, P, P], ctypes.c_int),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(L, name)
@@ -442,6 +445,41 @@ def bsa_attention_fwd_expanded_v(problem: Problem, q, k, v_bf16, row_ptr, col_id
     return out, (lse if want_lse else None)
 
 
+def bsa_prepare_v(problem: Problem, v, out=None):
+    """V [S, Hkv, 128] (bf16 or E4M3 codes) as the transposed bf16 tiles
+    [nb, Hkv, 128, 128] bsa_attention_fwd_prepared_v reads (head_dim = block_size =
+    128; E4M3 codes expanded exactly, v_scale not applied)."""
+    import torch
+    L = load_library()
+    nbytes = L.bsa_prepared_v_bytes(ctypes.byref(problem))
+    if nbytes == 0:
+        _check(L.bsa_prepare_v(ctypes.byref(problem), None, None, None))
+    if out is None:
+        out = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=v.device)
+    _check(L.bsa_prepare_v(ctypes.byref(problem), _ptr(_u8(v)), _ptr(out), _stream(v.device)))
+    return out
+
+
+def bsa_attention_fwd_prepared_v(problem: Problem, q, k, v_prepared, row_ptr, col_idx,
+                                 softmax_scale=None, q_scale=None, k_scale=None, v_scale=None,
+                                 want_lse=True, out=None, lse=None):
+    """bsa_attention_fwd with V given as bsa_prepare_v's tiles (bitwise the same results)."""
+    import torch
+    L = load_library()
+    S, Hq, D = q.shape
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty(S, Hq, D, dtype=torch.bfloat16, device=q.device)
+    if want_lse and lse is None:
+        lse = torch.empty(Hq, S, dtype=torch.float32, device=q.device)
+    _check(L.bsa_attention_fwd_prepared_v(
+        ctypes.byref(problem), _ptr(_u8(q)), _ptr(_u8(k)), _ptr(v_prepared), _ptr(q_scale),
+        _ptr(k_scale), _ptr(v_scale), _ptr(row_ptr), _ptr(col_idx), float(softmax_scale),
+        _ptr(out), _ptr(lse) if want_lse else None, _stream(q.device)))
+    return out, (lse if want_lse else None)
+
+
 def prefill_quest(q, k, v, block_size: int, params: SelectParams, granularity=BSA_SEL_PER_QHEAD,
                   q_scale=None, k_scale=None, v_scale=None, softmax_scale=None, export=False):
     """One layer on the Quest backbone: key bounds -> tile scores -> select -> attention.
@@ -462,7 +500,12 @@ def prefill(q, k, v, block_size: int, params: SelectParams, granularity=BSA_SEL_
     rescue = params.rescue_fraction > 0
     pool = bsa_pool(problem, q, k, q_scale, k_scale, want_norm=rescue, want_radius=rescue)
     sel = bsa_score_select(problem, params, pool, export=export)
-    if problem.dtype == BSA_FP8_E4M3:  # V codes expanded to bf16 once, attention reads those
+    if problem.dtype == BSA_FP8_E4M3 and problem.head_dim == 128 and problem.block_size == 128:
+        # V codes expanded once into the transposed bf16 tiles the P V products read
+        out, lse = bsa_attention_fwd_prepared_v(problem, q, k, bsa_prepare_v(problem, v),
+                                                sel.row_ptr, sel.col_idx, softmax_scale,
+                                                q_scale, k_scale, v_scale)
+    elif problem.dtype == BSA_FP8_E4M3:  # V codes expanded to bf16 once, attention reads those
         out, lse = bsa_attention_fwd_expanded_v(problem, q, k, bsa_expand_e4m3(problem, v),
                                                 sel.row_ptr, sel.col_idx, softmax_scale,
                                                 q_scale, k_scale, v_scale)

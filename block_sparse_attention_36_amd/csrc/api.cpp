@@ -586,4 +586,52 @@ bsa_status bsa_attention_fwd_expanded_v(const bsa_problem* problem, const void* 
                        "bsa_attention_fwd_expanded_v launch");
 }
 
+size_t bsa_prepared_v_bytes(const bsa_problem* problem) {
+  bsa::Shape sh;
+  if (check_problem(problem, sh) != BSA_OK || sh.D != 128 || sh.B != 128) return 0;
+  return (size_t)sh.nb * sh.Hkv * sh.D * sh.B * 2;
+}
+
+bsa_status bsa_prepare_v(const bsa_problem* problem, const void* v, void* v_prepared,
+                         void* hip_stream) {
+  bsa::Shape sh;
+  bsa_status st = check_problem(problem, sh);
+  if (st != BSA_OK) return st;
+  if (sh.D != 128 || sh.B != 128)
+    return fail(BSA_ERR_UNSUPPORTED, "prepared V tiles need head_dim = block_size = 128");
+  if (sh.S == 0) return ok();
+  if (!v || !v_prepared) return fail(BSA_ERR_INVALID_ARGUMENT, "v and v_prepared are required");
+  if (misaligned(v) || misaligned(v_prepared))
+    return fail(BSA_ERR_INVALID_ARGUMENT, "v and v_prepared must be 16-byte aligned");
+  return device_status(bsa::launch_prepare_v(sh, v, v_prepared, (hipStream_t)hip_stream),
+                       "bsa_prepare_v launch");
+}
+
+bsa_status bsa_attention_fwd_prepared_v(const bsa_problem* problem, const void* q, const void* k,
+                                        const void* v_prepared, const float* q_scale,
+                                        const float* k_scale, const float* v_scale,
+                                        const int32_t* row_ptr, const int32_t* col_idx,
+                                        float softmax_scale, void* out, float* lse,
+                                        void* hip_stream) {
+  bsa::Shape sh;
+  bsa_status st = check_problem(problem, sh);
+  if (st != BSA_OK) return st;
+  if (sh.D != 128 || sh.B != 128)
+    return fail(BSA_ERR_UNSUPPORTED, "prepared V tiles need head_dim = block_size = 128");
+  if (sh.S == 0) return ok();
+  if (!q || !k || !v_prepared || !row_ptr || !col_idx || !out)
+    return fail(BSA_ERR_INVALID_ARGUMENT,
+                "q, k, v_prepared, row_ptr, col_idx and out are required");
+  if (sh.fp8 && (!q_scale || !k_scale || !v_scale))
+    return fail(BSA_ERR_INVALID_ARGUMENT, "FP8 inputs need q_scale, k_scale and v_scale");
+  if (!std::isfinite(softmax_scale) || softmax_scale <= 0.f)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and > 0");
+  if (misaligned(q) || misaligned(k) || misaligned(v_prepared) || misaligned(out))
+    return fail(BSA_ERR_INVALID_ARGUMENT, "q, k, v_prepared and out must be 16-byte aligned");
+  return device_status(bsa::launch_attention(sh, q, k, v_prepared, q_scale, k_scale, v_scale,
+                                             row_ptr, col_idx, softmax_scale, out, lse,
+                                             (hipStream_t)hip_stream, 0, sh.fp8 != 0, true),
+                       "bsa_attention_fwd_prepared_v launch");
+}
+
 }  // extern "C"

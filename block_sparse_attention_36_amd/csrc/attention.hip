@@ -196,6 +196,57 @@ __device__ __forceinline__ void pv_tile(const unsigned char* vrow, const u32x4 (
   }
 }
 
+// Transposed V tiles (bsa_prepare_v's layout, D = B = 128): row d of the tile holds
+// dimension d of the block's keys, each 16-key group stored in the order
+// 0-3, 8-11, 4-7, 12-15, which is the order in which the probabilities sit in the
+// B operand (lane half hf holds keys 4hf + {0..3, 8..11} of each 16-key step).  So
+// the V^T operand of a step is one 16-byte read: row l % 32 (+ 32 dt), chunk
+// 4 kt2 + 2 sb + hf, behind the K tiles' swizzle (same 256-byte rows).
+template <int D, int B>
+__device__ __forceinline__ void pv_tile_t(const unsigned char* vtile, const u32x4 (&pk)[2],
+                                          f32x16 (&o)[D / 32], int kt2, int l) {
+  typedef WCfg<D, B> C;
+  static_assert(D == 128 && B == 128, "transposed V tiles are 128 x 128");
+  const int row = l & 31, hf = l >> 5, sw = swz<D>(row);
+  const unsigned char* rp = vtile + row * (B * 2);
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb) {
+    const int chunk = 4 * kt2 + 2 * sb + hf;
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt) {
+      const bf16x8 vf = *(const bf16x8*)(rp + dt * 32 * (B * 2) + ((chunk ^ sw) << 4));
+      o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, __builtin_bit_cast(bf16x8, pk[sb]),
+                                                      o[dt], 0, 0, 0);
+    }
+  }
+}
+
+// DMA of one transposed V tile: [D][B] bf16, contiguous for block j and kv head g
+// at ((j * Hkv + g) * D) * B; rows of 2B bytes land swizzled like the K tiles.
+template <int D, int B>
+struct VtTiles {
+  static constexpr int NW = B / 32;
+  static constexpr int ROW = B * 2;
+  static constexpr int TILE = D * ROW;
+  static constexpr int NI = TILE / (1024 * NW);
+  static_assert(NI >= 1 && TILE % (1024 * NW) == 0, "tile must split into 1 KiB DMAs");
+
+  static __device__ __forceinline__ void plan(int wave, int l, unsigned* off) {
+#pragma unroll
+    for (int n = 0; n < NI; ++n) {
+      const int p = (wave * NI + n) * 1024 + 16 * l;
+      const int r = p / ROW;
+      off[n] = (unsigned)(r * ROW + ((((p % ROW) >> 4) ^ swz<D>(r)) << 4));
+    }
+  }
+  static __device__ __forceinline__ void issue(const void* src, int Hkv, int g, int j,
+                                               unsigned char* dst, int wave, const unsigned* off) {
+    const unsigned char* base = (const unsigned char*)src + ((size_t)j * Hkv + g) * TILE;
+#pragma unroll
+    for (int n = 0; n < NI; ++n) dma16(base, off[n], lds_addr(dst + (wave * NI + n) * 1024));
+  }
+};
+
 // ---------------------------------------------------------------------------
 // Tiles of one workgroup and the order of one block's work:
 //   S(n), P(n) | wait V(n), barrier | request K(n+1) | O += V(n) P(n) |
@@ -269,12 +320,14 @@ struct WTiles {
   }
 };
 
-template <int D, int B, bool FP8, bool V16>
+template <int D, int B, bool FP8, bool V16, bool VT>
 __global__ __launch_bounds__(64 * (B / 32), 2) void attn_whole_kernel(AttnArgs a) {
   typedef WCfg<D, B> C;
   typedef WTiles<D, B, FP8> ST;
   typedef WTiles<D, B, false> SV;  // V tiles given as bf16 (E4M3 codes expanded beforehand)
+  typedef VtTiles<D, B> TV;        // V tiles given transposed (bsa_prepare_v)
   static_assert(!V16 || FP8, "bf16 V is the E4M3 path's option");
+  static_assert(!VT || (D == 128 && B == 128 && (V16 || !FP8)), "transposed V: 128 x 128 bf16");
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   const int tid = threadIdx.x, l = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -326,11 +379,17 @@ __global__ __launch_bounds__(64 * (B / 32), 2) void attn_whole_kernel(AttnArgs a
   auto blk = [](int j) { return j < 0 ? 0 : j; };
   unsigned doff[ST::NI];
   ST::plan(a, wave, l, doff);
-  unsigned voff[V16 ? SV::NI : 1];
-  if (V16) SV::plan(a, wave, l, voff);
-  // V(j): raw tile (then expanded in LDS), or the bf16 tile straight into place
+  unsigned voff[VT ? TV::NI : V16 ? SV::NI : 1];
+  if constexpr (VT)
+    TV::plan(wave, l, voff);
+  else if (V16)
+    SV::plan(a, wave, l, voff);
+  // V(j): raw tile (then expanded in LDS), or the bf16 tile straight into place,
+  // or the transposed bf16 tile
   auto issue_v = [&](int j) {
-    if (V16)
+    if constexpr (VT)
+      TV::issue(a.v, a.Hkv, g, j, lds + (FP8 ? ST::XV : ST::VBUF), wave, voff);
+    else if (V16)
       SV::issue(a, a.v, g, j, lds + ST::XV, wave, voff);
     else
       ST::issue(a, a.v, g, j, lds + ST::VBUF, wave, doff);
@@ -516,8 +575,13 @@ __global__ __launch_bounds__(64 * (B / 32), 2) void attn_whole_kernel(AttnArgs a
       lds_barrier();
     }
     if (FP8) vt = lds + ST::XV;
+    if constexpr (VT) {
 #pragma unroll
-    for (int kt2 = 0; kt2 < C::NKT; ++kt2) pv_tile<D, B>(vt + vrow0, pk[kt2], o, kt2, rlo, cb0);
+      for (int kt2 = 0; kt2 < C::NKT; ++kt2) pv_tile_t<D, B>(vt, pk[kt2], o, kt2, l);
+    } else {
+#pragma unroll
+      for (int kt2 = 0; kt2 < C::NKT; ++kt2) pv_tile<D, B>(vt + vrow0, pk[kt2], o, kt2, rlo, cb0);
+    }
 
     // ---- K(n + 1) has landed everywhere and V(n) is free: request V(n + 1)
     __builtin_amdgcn_s_setprio(0);
@@ -545,7 +609,7 @@ __global__ __launch_bounds__(64 * (B / 32), 2) void attn_whole_kernel(AttnArgs a
   }
 }
 
-template <int D, int B, bool FP8, bool V16 = false>
+template <int D, int B, bool FP8, bool V16 = false, bool VT = false>
 hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
   typedef WTiles<D, B, FP8> WT;
   static_assert(WT::LDS_BYTES <= 80 * 1024, "two workgroups per CU must fit the 160 KiB LDS");
@@ -557,13 +621,13 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
   (void)hipGetDevice(&dev);
   const uint64_t bit = 1ull << (dev & 63);
   if (!(attr_set.load(std::memory_order_acquire) & bit)) {
-    const hipError_t e = hipFuncSetAttribute((const void*)attn_whole_kernel<D, B, FP8, V16>,
+    const hipError_t e = hipFuncSetAttribute((const void*)attn_whole_kernel<D, B, FP8, V16, VT>,
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
                                              WT::LDS_BYTES);
     if (e != hipSuccess) return e;
     attr_set.fetch_or(bit, std::memory_order_acq_rel);
   }
-  hipLaunchKernelGGL((attn_whole_kernel<D, B, FP8, V16>), dim3(rows8 * 8 * G), dim3(WCfg<D, B>::NT),
+  hipLaunchKernelGGL((attn_whole_kernel<D, B, FP8, V16, VT>), dim3(rows8 * 8 * G), dim3(WCfg<D, B>::NT),
                      WT::LDS_BYTES, stream, a);
   return hipGetLastError();
 }
@@ -581,7 +645,70 @@ __global__ __launch_bounds__(256) void expand_e4m3_kernel(const u32x4* __restric
   out[2 * t + 1] = u32x4{c[0], c[1], d[0], d[1]};
 }
 
+// V [S, Hkv, 128] (bf16, or E4M3 codes expanded exactly) -> transposed bf16 tiles
+// [nb, Hkv, 128 dims, 128 keys], each 16-key group in the order 0-3, 8-11, 4-7,
+// 12-15 (the probabilities' order in the PV products), keys past S zero.  One
+// workgroup per (block, kv head): the tile's rows are loaded with 16-byte (8-byte
+// for codes) coalesced loads into LDS, then each thread gathers 8 keys of one
+// dimension and writes them as one 16-byte store, 16 threads per 256-byte row.
+template <bool FP8>
+__global__ __launch_bounds__(256) void prepare_v_kernel(const void* __restrict__ v,
+                                                        uint16_t* __restrict__ vt, int64_t S,
+                                                        int Hkv) {
+  constexpr int D = 128, B = 128, P = D + 2;  // padded LDS row (elements)
+  __shared__ uint16_t ts[B * P];
+  const int j = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int idx = it * 256 + tid, kk = idx >> 4, c = idx & 15;
+    const int64_t t = (int64_t)j * B + kk;
+    u32x4 w = u32x4{0u, 0u, 0u, 0u};
+    if (t < S) {
+      if (FP8) {
+        const u32x2 codes =
+            *(const u32x2*)((const uint8_t*)v + ((size_t)t * Hkv + g) * D + c * 8);
+        const u32x2 a = e4m3x4_to_bf16x4(codes[0]), b = e4m3x4_to_bf16x4(codes[1]);
+        w = u32x4{a[0], a[1], b[0], b[1]};
+      } else {
+        w = *(const u32x4*)((const uint16_t*)v + ((size_t)t * Hkv + g) * D + c * 8);
+      }
+    }
+    uint16_t* dst = ts + kk * P + c * 8;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      dst[2 * e] = (uint16_t)(w[e] & 0xFFFFu);
+      dst[2 * e + 1] = (uint16_t)(w[e] >> 16);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int idx = it * 256 + tid, d = idx >> 4, oc = idx & 15;
+    const int k0 = 16 * (oc >> 1) + 4 * (oc & 1);  // keys k0 + {0..3, 8..11}
+    unsigned y[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int ka = k0 + (e < 2 ? 2 * e : 2 * e + 4);
+      y[e] = (unsigned)ts[ka * P + d] | ((unsigned)ts[(ka + 1) * P + d] << 16);
+    }
+    *(u32x4*)(vt + (((size_t)j * Hkv + g) * D + d) * B + oc * 8) = u32x4{y[0], y[1], y[2], y[3]};
+  }
+}
+
 }  // namespace
+
+hipError_t launch_prepare_v(const Shape& sh, const void* v, void* vt, hipStream_t stream) {
+  if (sh.D != 128 || sh.B != 128) return hipErrorInvalidValue;
+  if (sh.nb == 0) return hipSuccess;
+  const dim3 grid((unsigned)sh.nb, (unsigned)sh.Hkv);
+  if (sh.fp8)
+    hipLaunchKernelGGL(prepare_v_kernel<true>, grid, dim3(256), 0, stream, v, (uint16_t*)vt, sh.S,
+                       sh.Hkv);
+  else
+    hipLaunchKernelGGL(prepare_v_kernel<false>, grid, dim3(256), 0, stream, v, (uint16_t*)vt,
+                       sh.S, sh.Hkv);
+  return hipGetLastError();
+}
 
 hipError_t launch_expand_e4m3(const Shape& sh, const void* codes, void* out, hipStream_t stream) {
   const int64_t n16 = sh.S * sh.Hkv * sh.D / 16;  // D is a multiple of 16
@@ -594,7 +721,8 @@ hipError_t launch_expand_e4m3(const Shape& sh, const void* codes, void* out, hip
 hipError_t launch_attention(const Shape& sh, const void* q, const void* k, const void* v,
                             const float* q_scale, const float* k_scale, const float* v_scale,
                             const int32_t* row_ptr, const int32_t* col_idx, float softmax_scale,
-                            void* out, float* lse, hipStream_t stream, int width, bool v16) {
+                            void* out, float* lse, hipStream_t stream, int width, bool v16,
+                            bool vt) {
   AttnArgs a;
   a.q = q;
   a.k = k;
@@ -613,6 +741,11 @@ hipError_t launch_attention(const Shape& sh, const void* q, const void* k, const
   a.per_group = sh.per_group;
   a.width = width;
   a.scale_log2 = softmax_scale * kLog2e;
+  if (vt) {
+    if (sh.D != 128 || sh.B != 128) return hipErrorInvalidValue;
+    return sh.fp8 ? launch_t<128, 128, true, true, true>(a, stream)
+                  : launch_t<128, 128, false, false, true>(a, stream);
+  }
 #define BSA_ATTN(DD, BB)                                                               \
   if (sh.D == DD && sh.B == BB)                                                       \
     return !sh.fp8 ? launch_t<DD, BB, false>(a, stream)                                \

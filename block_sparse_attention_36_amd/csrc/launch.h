@@ -70,7 +70,12 @@ hipError_t launch_attention(const Shape& sh, const void* q, const void* k, const
                             const float* q_scale, const float* k_scale, const float* v_scale,
                             const int32_t* row_ptr, const int32_t* col_idx, float softmax_scale,
                             void* out, float* lse, hipStream_t stream, int width = 0,
-                            bool v16 = false);
+                            bool v16 = false, bool vt = false);
+
+// V [S, Hkv, D] (bf16, or E4M3 codes expanded exactly) -> transposed bf16 tiles
+// [nb, Hkv, D, B] with each 16-key group in the probabilities' order; keys past S
+// are zero.  D = B = 128 only.
+hipError_t launch_prepare_v(const Shape& sh, const void* v, void* vt, hipStream_t stream);
 
 // E4M3 V codes [S, Hkv, D] -> their exact bf16 values in the same layout.
 hipError_t launch_expand_e4m3(const Shape& sh, const void* codes, void* out, hipStream_t stream);

@@ -74,7 +74,7 @@
 extern "C" {
 #endif
 
-#define BSA_ABI_VERSION 4
+#define BSA_ABI_VERSION 5
 
 typedef enum {
   BSA_OK = 0,
@@ -397,6 +397,41 @@ bsa_status bsa_expand_e4m3(const bsa_problem* problem, const void* v, void* v_bf
  */
 bsa_status bsa_attention_fwd_expanded_v(const bsa_problem* problem, const void* q, const void* k,
                                         const void* v_bf16, const float* q_scale,
+                                        const float* k_scale, const float* v_scale,
+                                        const int32_t* row_ptr, const int32_t* col_idx,
+                                        float softmax_scale, void* out, float* lse,
+                                        void* hip_stream);
+
+/*
+ * V in the form the P V products read, for bsa_attention_fwd_prepared_v (head_dim
+ * = block_size = 128 only).  Layout: bf16 [nb, Hkv, 128, 128], block j of kv head
+ * g a contiguous tile whose row d holds dimension d of the block's 128 keys, each
+ * group of 16 keys stored in the order 0-3, 8-11, 4-7, 12-15 (the order in which
+ * the probabilities of a 16-key step meet V in the bf16 matrix-core product);
+ * keys past seq_len are zero.  E4M3 codes are expanded exactly (v_scale is not
+ * applied; it stays an argument of the attention call).
+ *
+ * bsa_prepared_v_bytes: the size of that buffer (0 on invalid or unsupported
+ * problems).
+ * bsa_prepare_v:
+ *   v            [S, Hkv, D] bf16 or E4M3 codes (16-byte aligned).
+ *   v_prepared   out, bsa_prepared_v_bytes() bytes (16-byte aligned, owned by the
+ *                caller).
+ * BSA_ERR_UNSUPPORTED unless head_dim = block_size = 128.
+ */
+size_t bsa_prepared_v_bytes(const bsa_problem* problem);
+bsa_status bsa_prepare_v(const bsa_problem* problem, const void* v, void* v_prepared,
+                         void* hip_stream);
+
+/*
+ * bsa_attention_fwd_prepared_v -- bsa_attention_fwd (same passages, same
+ * arguments) with V given as bsa_prepare_v wrote it; the results equal
+ * bsa_attention_fwd's bit for bit.  Each V operand of the P V products is then
+ * one 16-byte LDS read instead of two transposing 8-byte reads.
+ * BSA_ERR_UNSUPPORTED unless head_dim = block_size = 128.
+ */
+bsa_status bsa_attention_fwd_prepared_v(const bsa_problem* problem, const void* q, const void* k,
+                                        const void* v_prepared, const float* q_scale,
                                         const float* k_scale, const float* v_scale,
                                         const int32_t* row_ptr, const int32_t* col_idx,
                                         float softmax_scale, void* out, float* lse,

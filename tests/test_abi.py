@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.bsa_abi_version() == 4
+    assert lib.bsa_abi_version() == 5
     assert lib.bsa_status_string(0) == b"ok"
     assert lib.bsa_status_string(3) == b"CSR capacity too small"
 

@@ -142,6 +142,9 @@ ENTRY_POINTS = {
     "bsa_attention_fwd_expanded_v": lambda L, P, S: L.bsa_attention_fwd_expanded_v(
         P, *([None] * 8), 0.125, None, None, None),
     "bsa_expand_e4m3": lambda L, P, S: L.bsa_expand_e4m3(P, None, None, None),
+    "bsa_prepare_v": lambda L, P, S: L.bsa_prepare_v(P, None, None, None),
+    "bsa_attention_fwd_prepared_v": lambda L, P, S: L.bsa_attention_fwd_prepared_v(
+        P, *([None] * 8), 0.125, None, None, None),
     "bsa_pool_key_bounds": lambda L, P, S: L.bsa_pool_key_bounds(P, *([None] * 5)),
     "bsa_quest_scores": lambda L, P, S: L.bsa_quest_scores(P, *([None] * 6), 10**12, None),
     "bsa_select_scores": lambda L, P, S: L.bsa_select_scores(P, S, None, None, None, 10**9,

@@ -365,6 +365,63 @@ def test_expanded_v_attention_equals_the_codes_path(cfg):
     assert torch.equal(lse0, lse1)
 
 
+# the prepared (transposed) V tiles: bf16 and E4M3, one list per head and per GQA
+# group, ragged tails, and the 1M-token layer the benchmark runs on them
+PREPARED_V = [
+    scaled(config_by_name("dual128k"), 4096 + 77, num_q_heads=8, num_kv_heads=2,
+           name="prepared-bf16"),
+    scaled(config_by_name("gqa32k"), 2 * 4096 + 5, num_q_heads=8, num_kv_heads=2,
+           name="prepared-bf16-topk"),
+    scaled(config_by_name("dual128k_fp8"), 4096 + 77, num_q_heads=8, num_kv_heads=2,
+           name="prepared-fp8"),
+    scaled(config_by_name("msa1m"), 8192 + 1, num_q_heads=16, num_kv_heads=2,
+           name="prepared-fp8-group"),
+    config_by_name("msa1m")]
+
+
+@pytest.mark.parametrize("cfg", PREPARED_V, ids=[c.name for c in PREPARED_V])
+def test_prepared_v_attention_equals_the_plain_path(cfg):
+    """bsa_prepare_v writes every value of V (E4M3 codes decoded exactly) at its place
+    in the transposed tiles, zero past the sequence, and attention on them equals
+    bsa_attention_fwd on V as given bit for bit (outputs and log-sum-exp), so the
+    oracle parity of the plain path carries over."""
+    _gpu_or_skip()
+    import block_sparse_attention_36_amd as bsa
+    import bsa_check as K
+    print(f"[prepared-v] {cfg.name} S={cfg.seq_len} Hq={cfg.num_q_heads} "
+          f"Hkv={cfg.num_kv_heads} {cfg.dtype}", flush=True)
+    inp = generate(cfg, "cpu" if cfg.seq_len < 100000 else "cuda").to("cuda")
+    problem = bsa.make_problem(inp.q, inp.k, cfg.block_size, K.granularity_code(cfg))
+    params = K.lib_params(cfg)
+    pool = bsa.bsa_pool(problem, inp.q, inp.k, inp.q_scale, inp.k_scale)
+    sel = bsa.bsa_score_select(problem, params, pool)
+    vp = bsa.bsa_prepare_v(problem, inp.v)
+    # the tiles against the layout, from V decoded by torch: [nb, Hkv, 128 dims, 128 keys]
+    # with each 16-key group stored as keys 0-3, 8-11, 4-7, 12-15, zero past S
+    S, Hkv, D = inp.v.shape
+    nb = -(-S // 128)
+    vf = (inp.v.view(torch.float8_e4m3fn).float() if cfg.dtype == "fp8" else inp.v.float())
+    vpad = torch.zeros(nb * 128, Hkv, D, device="cuda")
+    vpad[:S] = vf
+    order = torch.tensor([0, 1, 2, 3, 8, 9, 10, 11, 4, 5, 6, 7, 12, 13, 14, 15], device="cuda")
+    perm = (torch.arange(8, device="cuda")[:, None] * 16 + order[None, :]).reshape(-1)
+    want = vpad.view(nb, 128, Hkv, D)[:, perm].permute(0, 2, 3, 1).to(torch.bfloat16)
+    assert torch.equal(vp.view(nb, Hkv, D, 128).view(torch.int16),
+                       want.contiguous().view(torch.int16))
+    del vf, vpad, want
+    scale = 1.0 / math.sqrt(cfg.head_dim)
+    out0, lse0 = bsa.bsa_attention_fwd(problem, inp.q, inp.k, inp.v, sel.row_ptr, sel.col_idx,
+                                       scale, inp.q_scale, inp.k_scale, inp.v_scale)
+    out1, lse1 = bsa.bsa_attention_fwd_prepared_v(problem, inp.q, inp.k, vp, sel.row_ptr,
+                                                  sel.col_idx, scale, inp.q_scale, inp.k_scale,
+                                                  inp.v_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out0.view(torch.int16), out1.view(torch.int16))
+    assert torch.equal(lse0, lse1)
+    del inp, pool, sel, vp, out0, out1, lse0, lse1
+    torch.cuda.empty_cache()
+
+
 RANDOM = random_layers(48)
 
 
