@@ -21,7 +21,11 @@ CASES = [scaled(config_by_name("gqa32k"), 4096 + 77, num_q_heads=8, num_kv_heads
          scaled(config_by_name("msa1m"), 4096 + 70, num_q_heads=8, num_kv_heads=2),
          scaled(config_by_name("quest64k"), 4096 + 5, num_q_heads=8, num_kv_heads=2),
          scaled(config_by_name("sigma64k"), 4096 + 33, num_q_heads=8, num_kv_heads=2,
-                name="padded-sigma64k")]
+                name="padded-sigma64k"),
+         scaled(config_by_name("msa1m"), 4096 + 70, num_q_heads=8, num_kv_heads=2,
+                name="prepared-msa1m"),
+         scaled(config_by_name("dual128k"), 4096 + 100, num_q_heads=8, num_kv_heads=2,
+                name="prepared-dual128k")]
 
 
 def _gpu_or_skip():
@@ -39,6 +43,7 @@ class Layer:
         self.cfg, self.inp, self.noalloc = cfg, inp, noalloc
         self.quest = cfg.backbone == "quest"
         self.padded = cfg.name.startswith("padded")
+        self.prepared = cfg.name.startswith("prepared")
         self.problem = bsa.make_problem(inp.q, inp.k, cfg.block_size, K.granularity_code(cfg))
         self.params = K.lib_params(cfg)
         if self.quest:
@@ -53,7 +58,8 @@ class Layer:
         self.out = torch.empty(S, Hq, D, dtype=torch.bfloat16, device="cuda")
         self.lse = torch.empty(Hq, S, dtype=torch.float32, device="cuda")
         self.v16 = (torch.empty(inp.v.shape, dtype=torch.bfloat16, device="cuda")
-                    if cfg.dtype == "fp8" else None)
+                    if cfg.dtype == "fp8" and not self.prepared else None)
+        self.vp = bsa.bsa_prepare_v(self.problem, inp.v) if self.prepared else None
 
     def run(self):
         i, p = self.inp, self.problem
@@ -72,7 +78,12 @@ class Layer:
                 return
             select = bsa.bsa_score_select_noalloc if self.noalloc else bsa.bsa_score_select
             sel = select(p, self.params, self.pool, buffers=self.bufs)
-        if self.v16 is not None:
+        if self.vp is not None:
+            bsa.bsa_prepare_v(p, i.v, out=self.vp)
+            bsa.bsa_attention_fwd_prepared_v(p, i.q, i.k, self.vp, sel.row_ptr, sel.col_idx,
+                                             scale, i.q_scale, i.k_scale, i.v_scale,
+                                             out=self.out, lse=self.lse)
+        elif self.v16 is not None:
             bsa.bsa_expand_e4m3(p, i.v, out=self.v16)
             bsa.bsa_attention_fwd_expanded_v(p, i.q, i.k, self.v16, sel.row_ptr, sel.col_idx,
                                              scale, i.q_scale, i.k_scale, i.v_scale,
