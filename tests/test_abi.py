@@ -339,3 +339,40 @@ def test_expanded_v_entry_points_reject_bf16_problems_and_missing_pointers(lib):
     assert lib.bsa_expand_e4m3(ctypes.byref(e8), None, None, None) == 0
     assert lib.bsa_attention_fwd_expanded_v(ctypes.byref(e8), None, None, None, None, None, None,
                                             None, None, 0.1, None, None, None) == 0
+
+
+def test_prepared_v_entry_points_need_128_by_128_and_validate(lib):
+    """The prepared V tiles exist for head_dim = block_size = 128 only (bf16 or E4M3):
+    their size is nb * Hkv * 128 * 128 bf16, other shapes report 0 bytes and
+    BSA_ERR_UNSUPPORTED, and every check fails before a device call."""
+    p = _prob()  # S 4096, 8/2 heads, D 128, B 128, bf16
+    nb = 4096 // 128
+    assert lib.bsa_prepared_v_bytes(ctypes.byref(p)) == nb * 2 * 128 * 128 * 2
+    r = _prob(seq_len=4096 + 77)  # ragged: the last block's tile is whole
+    assert lib.bsa_prepared_v_bytes(ctypes.byref(r)) == (nb + 1) * 2 * 128 * 128 * 2
+    for kw in (dict(head_dim=64), dict(block_size=64), dict(head_dim=64, block_size=64)):
+        q = _prob(**kw)
+        assert lib.bsa_prepared_v_bytes(ctypes.byref(q)) == 0
+        assert lib.bsa_prepare_v(ctypes.byref(q), FAKE, FAKE, None) == 2
+        st = lib.bsa_attention_fwd_prepared_v(ctypes.byref(q), FAKE, FAKE, FAKE, None, None, None,
+                                              FAKE, FAKE, 0.1, FAKE, None, None)
+        assert st == 2 and b"128" in lib.bsa_last_error()
+    assert lib.bsa_prepared_v_bytes(ctypes.byref(_prob(head_dim=96))) == 0  # invalid problem
+    assert lib.bsa_prepare_v(ctypes.byref(p), None, FAKE, None) == 1
+    assert lib.bsa_prepare_v(ctypes.byref(p), FAKE, ctypes.c_void_p(0x1008), None) == 1
+    assert b"aligned" in lib.bsa_last_error()
+    st = lib.bsa_attention_fwd_prepared_v(ctypes.byref(p), FAKE, FAKE, None, None, None, None,
+                                          FAKE, FAKE, 0.1, FAKE, None, None)
+    assert st == 1
+    st = lib.bsa_attention_fwd_prepared_v(ctypes.byref(p), FAKE, FAKE, FAKE, None, None, None,
+                                          FAKE, FAKE, 0.0, FAKE, None, None)
+    assert st == 1
+    q8 = _prob(dtype=bsa.BSA_FP8_E4M3)
+    assert lib.bsa_prepared_v_bytes(ctypes.byref(q8)) == nb * 2 * 128 * 128 * 2
+    st = lib.bsa_attention_fwd_prepared_v(ctypes.byref(q8), FAKE, FAKE, FAKE, None, FAKE, FAKE,
+                                          FAKE, FAKE, 0.1, FAKE, None, None)
+    assert st == 1 and b"scale" in lib.bsa_last_error()
+    e = _prob(seq_len=0)
+    assert lib.bsa_prepare_v(ctypes.byref(e), None, None, None) == 0
+    assert lib.bsa_attention_fwd_prepared_v(ctypes.byref(e), None, None, None, None, None, None,
+                                            None, None, 0.1, None, None, None) == 0
