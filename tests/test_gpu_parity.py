@@ -441,3 +441,15 @@ def test_random_small_layers_parity(cfg):
           f"max_abs={rep.max_abs:.3g} mean_abs={rep.mean_abs:.3g} lse={rep.lse_max:.3g}",
           flush=True)
     assert rep.ambiguous_rows <= max(1, rep.rows_checked // 100)
+    if cfg.head_dim == 128 and cfg.block_size == 128:
+        # attention on the prepared V tiles gives the checked outputs bit for bit
+        import block_sparse_attention_36_amd as bsa
+        problem = bsa.make_problem(inp.q, inp.k, cfg.block_size, K.granularity_code(cfg))
+        rp = torch.from_numpy(run.row_ptr.astype(np.int32)).to("cuda")
+        ci = torch.from_numpy(run.col_idx.astype(np.int32)).to("cuda")
+        out, lse = bsa.bsa_attention_fwd_prepared_v(
+            problem, inp.q, inp.k, bsa.bsa_prepare_v(problem, inp.v), rp, ci,
+            1.0 / math.sqrt(cfg.head_dim), inp.q_scale, inp.k_scale, inp.v_scale)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), run.out.view(torch.int16))
+        assert torch.equal(lse, run.lse)
