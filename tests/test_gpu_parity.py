@@ -262,6 +262,26 @@ def test_fp8_zero_blocks_with_zero_scales():
     assert torch.isfinite(run.out.float()).all() and not torch.isnan(run.lse).any()
     rep = K.check_all(cfg, inp, run)
     print(f"  zero blocks: max_abs={rep.max_abs:.3g} lse={rep.lse_max:.3g}", flush=True)
+    # zero value blocks with scale 0 as well, through the prepared V tiles: the same
+    # bytes as the codes path
+    import block_sparse_attention_36_amd as bsa
+    for blk in (2, cfg.num_blocks - 1):
+        t0, t1 = blk * cfg.block_size, min(cfg.seq_len, (blk + 1) * cfg.block_size)
+        inp.v[t0:t1, 1] = 0
+        inp.v_scale[1, blk] = 0.0
+    problem = bsa.make_problem(inp.q, inp.k, cfg.block_size, K.granularity_code(cfg))
+    rp = torch.from_numpy(run.row_ptr.astype(np.int32)).to("cuda")
+    ci = torch.from_numpy(run.col_idx.astype(np.int32)).to("cuda")
+    scale = 1.0 / math.sqrt(cfg.head_dim)
+    out0, lse0 = bsa.bsa_attention_fwd(problem, inp.q, inp.k, inp.v, rp, ci, scale,
+                                       inp.q_scale, inp.k_scale, inp.v_scale)
+    out1, lse1 = bsa.bsa_attention_fwd_prepared_v(problem, inp.q, inp.k,
+                                                  bsa.bsa_prepare_v(problem, inp.v), rp, ci,
+                                                  scale, inp.q_scale, inp.k_scale, inp.v_scale)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out0.float()).all() and not torch.isnan(lse0).any()
+    assert torch.equal(out0.view(torch.int16), out1.view(torch.int16))
+    assert torch.equal(lse0, lse1)
 
 
 def test_empty_sequence_is_a_no_op():
