@@ -547,11 +547,18 @@ __device__ void topk_reg(const RowKeys<SPL>& r, int nsl, int nc, int k, unsigned
 // mass probabilities would not fit in registers at 128 slots).  SIG compiles the
 // sigma gate's per-row part (its extra state stays out of the other forms).
 // (the widest forms are held to the registers of two waves per SIMD, the 32-slot
-// form with every branch to three: a wave with its SIMD to itself waits out every
-// load and reduction latency of its row, and a few spilled registers cost less)
+// form with every branch to three, the 64-slot top-k-only one to four and the
+// 16-slot one to five: a wave with its SIMD to itself waits out every load and
+// reduction latency of its row, and a few spilled registers cost less; at 16 slots
+// the fifth wave takes 9 % off the selection of 128K-token layers, at 64 the
+// fourth 2 % off that of 1M-token layers)
 template <int SPL, bool FULL, bool SIG>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
-    (SPL >= 128 || (SPL == 64 && FULL && !SIG)) ? 2 : (SPL == 32 && FULL) ? 3 : 1)))
+    (SPL >= 128 || (SPL == 64 && FULL && !SIG)) ? 2
+    : (SPL == 32 && FULL)                        ? 3
+    : (SPL == 64 && !FULL)                       ? 4
+    : (SPL == 16 && FULL)                        ? 5
+                                                 : 1)))
 void select_reg_kernel(SelArgs a) {
   clear_overflow(a);
   const bool use_b = FULL && a.use_b, use_p = FULL && a.use_p;
@@ -578,8 +585,10 @@ void select_reg_kernel(SelArgs a) {
   // together (indices clamped into the row, one wait per chunk) rather than one
   // load and one wait per slot
   // (32 slots per chunk for the 32- and 64-slot top-k-only forms, 16 for the
-  // 128-slot one, whose 256 registers leave no room for more, 8 for the others)
-  constexpr int CH = SPL <= 16 ? SPL : (!FULL ? (SPL >= 128 ? 16 : SPL > 32 ? 32 : SPL) : 8);
+  // 128-slot one, whose 256 registers leave no room for more, the whole row up to
+  // 16 slots but 8 for the other forms with every branch)
+  constexpr int CH = FULL ? (SPL <= 8 ? SPL : 8)
+                          : (SPL <= 16 ? SPL : SPL >= 128 ? 16 : SPL > 32 ? 32 : SPL);
 #pragma unroll
   for (int e0 = 0; e0 < SPL; e0 += CH) {
 #pragma unroll
